@@ -1,0 +1,195 @@
+/*
+ * oracle.c -- plain C CPU oracle for the int4 MoE feed-forward layer.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, smoke() and the bench's
+ * cpu_baseline leg, never by the product library. It shares no code with it.
+ *
+ * Two things live here, both written as the plainest loops:
+ *
+ *  1. oracle_quantize_int4: the int4 group quantizer printed as
+ *     int4_row_quantize on the discosf.com page "1 卡跑通 Llama 4", section
+ *     "FP8 / Int4 混合量化". Per group of `group` consecutive fp32 weights:
+ *     scale = max(max|w|, 1e-6f) / 8, code = clamp(round_half_even(w / scale),
+ *     -8, 7). fp32 division (IEEE, correctly rounded) and rintf under the
+ *     default round-to-nearest-even mode. Built with -ffp-contract=off and
+ *     without fast-math.
+ *
+ *  2. oracle_moe_token: the MoE layer for ONE token, as a per-token loop
+ *     (discosf.com page, section "混合专家路由"): router logits, top-k
+ *     (ties to the lower expert id), sigmoid gates, and for each chosen expert
+ *     the SwiGLU FFN (docs.ifdog.com page "Llama 开源模型系列", section
+ *     "SwiGLU：门控激活的数学") weighted by its gate, then plus the shared
+ *     expert. Everything in double; logits rounded to float before the top-k
+ *     choice (the choice is taken in fp32). Routed weights are dequantized
+ *     on the fly as code * scale, one weight at a time.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- quantizer */
+
+void oracle_quantize_int4(const float *w, int64_t rows, int64_t K, int64_t group,
+                          int8_t *codes, float *scales)
+{
+    const int64_t ngroups = K / group;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t g = 0; g < ngroups; ++g) {
+            const float *src = w + r * K + g * group;
+            int8_t *dst = codes + r * K + g * group;
+            float m = 0.0f;
+            for (int64_t i = 0; i < group; ++i) {
+                float a = fabsf(src[i]);
+                if (a > m) m = a;
+            }
+            float s = (m < 1e-6f ? 1e-6f : m) / 8.0f;
+            scales[r * ngroups + g] = s;
+            for (int64_t i = 0; i < group; ++i) {
+                float q = rintf(src[i] / s);
+                if (q < -8.0f) q = -8.0f;
+                if (q > 7.0f) q = 7.0f;
+                dst[i] = (int8_t)q;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ helpers */
+
+static double bf16_to_double(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+static double silu(double z) { return z * sigmoid(z); }
+
+/* w_hat[row][j] of an int4 matrix with `cols` columns */
+static double dq(const int8_t *c, const float *s, int64_t cols, int64_t group,
+                 int64_t row, int64_t j)
+{
+    return (double)c[row * cols + j] * (double)s[row * (cols / group) + j / group];
+}
+
+/* One SwiGLU expert with int4 weights on one token:
+ *   a[n] = sum_j x[j] W1[n][j],  b[n] = sum_j x[j] W3[n][j]   (W1, W3: [h, d])
+ *   u[n] = silu(a[n]) * b[n]
+ *   o[m] = sum_n u[n] W2[m][n]                                  (W2: [d, h]) */
+void oracle_swiglu_int4_token(const double *x, int64_t d, int64_t h, int64_t group,
+                              const int8_t *c1, const float *s1,
+                              const int8_t *c3, const float *s3,
+                              const int8_t *c2, const float *s2,
+                              double *u, double *o)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < h; ++n) {
+        double a = 0.0, b = 0.0;
+        for (int64_t j = 0; j < d; ++j) {
+            a += x[j] * dq(c1, s1, d, group, n, j);
+            b += x[j] * dq(c3, s3, d, group, n, j);
+        }
+        u[n] = silu(a) * b;
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < d; ++m) {
+        double acc = 0.0;
+        for (int64_t n = 0; n < h; ++n)
+            acc += u[n] * dq(c2, s2, h, group, m, n);
+        o[m] = acc;
+    }
+}
+
+/* The same expert with bf16 weights (the shared expert). */
+void oracle_swiglu_bf16_token(const double *x, int64_t d, int64_t h,
+                              const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                              double *u, double *o)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < h; ++n) {
+        double a = 0.0, b = 0.0;
+        for (int64_t j = 0; j < d; ++j) {
+            a += x[j] * bf16_to_double(w1[n * d + j]);
+            b += x[j] * bf16_to_double(w3[n * d + j]);
+        }
+        u[n] = silu(a) * b;
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < d; ++m) {
+        double acc = 0.0;
+        for (int64_t n = 0; n < h; ++n)
+            acc += u[n] * bf16_to_double(w2[m * h + n]);
+        o[m] = acc;
+    }
+}
+
+/* logits[e] = (float)(sum_j x[j] Wr[e][j] + b[e]), accumulated in double */
+void oracle_router_token(const double *x, const float *wr, const float *bias,
+                         int64_t E, int64_t d, float *logits)
+{
+    for (int64_t e = 0; e < E; ++e) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < d; ++j)
+            acc += x[j] * (double)wr[e * d + j];
+        if (bias) acc += (double)bias[e];
+        logits[e] = (float)acc;
+    }
+}
+
+/* k rounds of "largest remaining logit, lower id on ties" */
+void oracle_topk_token(const float *logits, int64_t E, int32_t k, int32_t *ids)
+{
+    for (int32_t j = 0; j < k; ++j) {
+        int32_t best = -1;
+        for (int64_t e = 0; e < E; ++e) {
+            int taken = 0;
+            for (int32_t i = 0; i < j; ++i)
+                if (ids[i] == (int32_t)e) taken = 1;
+            if (taken) continue;
+            if (best < 0 || logits[e] > logits[best]) best = (int32_t)e;
+        }
+        ids[j] = best;
+    }
+}
+
+/*
+ * The whole layer for one token. Expert e's weights are c1[e], s1[e], ...;
+ * an expert the token does not choose may be NULL. If forced_ids is not NULL
+ * it replaces the top-k choice. Returns 0, or -1 if a chosen expert is NULL
+ * or an id is out of range.
+ *   y[m] = sum_j gate_j * expert_{id_j}(x)[m]  +  shared(x)[m]
+ * scratch: u [h] and o [d] doubles.
+ */
+int oracle_moe_token(const double *x, int64_t d, int64_t h, int64_t E, int32_t k,
+                     int64_t group, const float *wr, const float *bias,
+                     const int8_t *const *c1, const float *const *s1,
+                     const int8_t *const *c3, const float *const *s3,
+                     const int8_t *const *c2, const float *const *s2,
+                     const uint16_t *sh1, const uint16_t *sh3, const uint16_t *sh2,
+                     const int32_t *forced_ids,
+                     float *logits, int32_t *ids, double *gates,
+                     double *u, double *o, double *y)
+{
+    oracle_router_token(x, wr, bias, E, d, logits);
+    if (forced_ids)
+        for (int32_t j = 0; j < k; ++j) ids[j] = forced_ids[j];
+    else
+        oracle_topk_token(logits, E, k, ids);
+
+    for (int64_t m = 0; m < d; ++m) y[m] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+        int32_t e = ids[j];
+        if (e < 0 || e >= E || !c1[e] || !c3[e] || !c2[e]) return -1;
+        gates[j] = sigmoid((double)logits[e]);
+        oracle_swiglu_int4_token(x, d, h, group, c1[e], s1[e], c3[e], s3[e],
+                                 c2[e], s2[e], u, o);
+        for (int64_t m = 0; m < d; ++m) y[m] += gates[j] * o[m];
+    }
+    oracle_swiglu_bf16_token(x, d, h, sh1, sh3, sh2, u, o);
+    for (int64_t m = 0; m < d; ++m) y[m] += o[m];
+    return 0;
+}
