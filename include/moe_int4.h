@@ -1,0 +1,172 @@
+/*
+ * moe_int4.h -- C ABI of the MI355X (gfx950) int4 Mixture-of-Experts
+ * feed-forward layer.
+ *
+ * The layer (discosf.com page "1 卡跑通 Llama 4", section "混合专家路由"):
+ * a router scores every expert for each token, the top-k experts are chosen,
+ * each chosen expert's SwiGLU FFN runs on its tokens and its output is added
+ * back to the token weighted by the token's gate for that expert, and the
+ * output of a shared expert that every token passes through is added last.
+ * Expert FFN (docs.ifdog.com page "Llama 开源模型系列", section
+ * "SwiGLU：门控激活的数学"): (Swish(x W1^T) * (x W3^T)) W2^T with
+ * Swish(z) = z * sigmoid(z). Routed-expert weights are int4 in groups of 128
+ * (same discosf.com page, section "FP8 / Int4 混合量化"); activations and the
+ * shared expert stay bf16 (lshu.cn page, section "量化环节").
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers on the current HIP device, owned
+ *     by the caller; the library never allocates or frees them and keeps no
+ *     pointer after the call returns. `stream` is a hipStream_t (NULL = the
+ *     default stream); work is enqueued asynchronously on it.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Matrices are row-major. Weights are stored "nt": one row per output
+ *     feature, the reduction dimension contiguous (W1, W3: [h, d]; W2: [d, h]).
+ *   - Return value: MOE_OK, or an error code; nothing is enqueued when a
+ *     validation error is returned. Faults during execution surface at the
+ *     caller's next synchronisation. No C++ exception crosses the ABI.
+ *     moe_last_error() gives a thread-local detail string for the last error.
+ *   - Calls on one stream are ordered; concurrent calls on different streams
+ *     must use distinct workspaces.
+ */
+#ifndef MOE_INT4_H
+#define MOE_INT4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_INT4_ABI_VERSION 1
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,        /* bad shape, null or misaligned pointer */
+    MOE_ERR_UNSUPPORTED_DEVICE = 2, /* current device is not gfx950 */
+    MOE_ERR_HIP = 3,                /* a HIP runtime call failed */
+    MOE_ERR_WORKSPACE = 4           /* workspace missing or too small */
+};
+
+enum moe_path {
+    MOE_PATH_AUTO = 0,     /* decode path for small batches, prefill otherwise */
+    MOE_PATH_PREFILL = 1,  /* grouped int4 GEMMs on MFMA */
+    MOE_PATH_DECODE = 2    /* HBM-streaming GEMV over the touched experts */
+};
+
+/* Limits checked by validation. */
+#define MOE_GROUP_SIZE 128     /* the only supported quantization group */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOP_K 16
+
+/* Static description of an error code; never NULL. */
+const char *moe_status_string(int status);
+
+/* Detail text of the last error returned on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+/* MOE_INT4_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+/* MOE_OK if the current HIP device is a gfx950, else MOE_ERR_UNSUPPORTED_DEVICE
+ * (or MOE_ERR_HIP if there is no device). */
+int moe_device_check(void);
+
+/*
+ * Int4 group quantizer (discosf.com page, section "FP8 / Int4 混合量化",
+ * int4_row_quantize). For each group of `group_size` consecutive weights of a
+ * row: scale = max(max|w|, 1e-6f) / 8, code = clamp(round_half_even(w / scale),
+ * -8, 7), in fp32 with a correctly rounded division.
+ *
+ *   w       fp32 [rows, K], K % group_size == 0, 16-byte aligned
+ *   q       out, uint8 [rows, K/2]: byte j of a row holds code 2j in its low
+ *           nibble and code 2j+1 in its high nibble, 4-bit two's complement
+ *   scales  out, fp32 [rows, K/group_size]
+ *   group_size  must be MOE_GROUP_SIZE
+ */
+int moe_quantize_int4(const float *w, int64_t rows, int64_t K, int32_t group_size,
+                      uint8_t *q, float *scales, void *stream);
+
+typedef struct moe_dims {
+    int64_t T;      /* tokens, >= 1 */
+    int64_t d;      /* model dim, multiple of 128 */
+    int64_t E;      /* routed experts, 1..MOE_MAX_EXPERTS */
+    int64_t h;      /* expert hidden dim, multiple of 128 */
+    int32_t top_k;  /* 1..min(E, MOE_MAX_TOP_K) */
+    int32_t group_size; /* must be MOE_GROUP_SIZE */
+} moe_dims;
+
+/* Routed experts in the layout moe_quantize_int4 writes, experts stacked:
+ *   w1q, w3q [E, h, d/2] bytes   w1s, w3s [E, h, d/128] fp32
+ *   w2q      [E, d, h/2] bytes   w2s      [E, d, h/128] fp32 */
+typedef struct moe_experts_int4 {
+    const uint8_t *w1q, *w3q, *w2q;
+    const float *w1s, *w3s, *w2s;
+} moe_experts_int4;
+
+/* Shared expert, bf16: s1, s3 [h, d]; s2 [d, h]. */
+typedef struct moe_shared_bf16 {
+    const uint16_t *s1, *s3, *s2;
+} moe_shared_bf16;
+
+/* Bytes of device workspace moe_forward / moe_route need for `dims`
+ * (0 if dims are invalid). */
+size_t moe_forward_workspace_bytes(const moe_dims *dims);
+
+/*
+ * The MoE feed-forward layer.
+ *   x          bf16 [T, d]
+ *   router_w   fp32 [E, d]; logit[t,e] = sum_j x[t,j] router_w[e,j] (+ router_b[e])
+ *   router_b   fp32 [E] or NULL
+ *   experts    routed int4 experts (see moe_experts_int4)
+ *   shared     shared bf16 expert
+ *   y          out, bf16 [T, d]:
+ *              y[t] = shared(x_t) + sum_j gate[t,j] * expert_{id[t,j]}(x_t)
+ *   topk_ids   out, int32 [T, top_k] or NULL: chosen experts by descending
+ *              logit, ties to the lower id
+ *   topk_gates out, fp32 [T, top_k] or NULL: sigmoid of the chosen logits
+ *   workspace  device buffer of >= moe_forward_workspace_bytes(dims) bytes,
+ *              256-byte aligned; contents are scratch
+ * Accumulation is fp32; the only roundings beyond fp32 are the bf16 inputs of
+ * the matrix cores (dequantized weights, SwiGLU hidden rows) and the bf16 y.
+ */
+int moe_forward(const moe_dims *dims, const uint16_t *x, const float *router_w,
+                const float *router_b, const moe_experts_int4 *experts,
+                const moe_shared_bf16 *shared, uint16_t *y, int32_t *topk_ids,
+                float *topk_gates, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* moe_forward with an explicit path (enum moe_path). */
+int moe_forward_path(const moe_dims *dims, const uint16_t *x, const float *router_w,
+                     const float *router_b, const moe_experts_int4 *experts,
+                     const moe_shared_bf16 *shared, uint16_t *y, int32_t *topk_ids,
+                     float *topk_gates, int32_t path, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace moe_route alone needs (a prefix of the forward
+ * workspace; 0 if dims are invalid; dims->h is ignored). */
+size_t moe_route_workspace_bytes(const moe_dims *dims);
+
+/*
+ * Routing alone: router logits, top-k + sigmoid gates, and the token->expert
+ * dispatch the grouped GEMMs use (discosf.com page, section "混合专家路由").
+ * Pairs are p = t * top_k + j. Every output except topk_ids/topk_gates may be
+ * NULL.
+ *   logits   out, fp32 [T, E] (bias included)
+ *   counts   out, int32 [E]: pairs routed to each expert
+ *   offsets  out, int32 [E+1]: exclusive prefix sum of counts
+ *   perm     out, int32 [T*top_k]: perm[slot] = pair; slots of expert e are
+ *            offsets[e]..offsets[e+1]-1, pairs in ascending order
+ *   inv      out, int32 [T*top_k]: inv[pair] = slot
+ *   workspace >= moe_route_workspace_bytes(dims) bytes, 256-byte aligned
+ */
+int moe_route(const moe_dims *dims, const uint16_t *x, const float *router_w,
+              const float *router_b, int32_t *topk_ids, float *topk_gates,
+              float *logits, int32_t *counts, int32_t *offsets, int32_t *perm,
+              int32_t *inv, void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_INT4_H */

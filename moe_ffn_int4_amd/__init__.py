@@ -1,0 +1,282 @@
+"""MI355X (gfx950) int4 Mixture-of-Experts feed-forward layer.
+
+Thin ctypes binding over ``libmoe_int4.so`` (C ABI in ``include/moe_int4.h``).
+This module only checks and marshals arguments: torch provides device memory
+and the current HIP stream, and every step of the layer runs in the library's
+HIP kernels. There is no fallback: if the library is missing, importing the
+functions below raises.
+
+    q, s = quantize_int4(w_fp32_cuda)                 # int4 group quantizer
+    y = forward(x, router_w, router_b, experts, shared, top_k)
+    r = route(x, router_w, router_b, top_k)           # routing/dispatch only
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_int4.so")
+GROUP = 128
+PATHS = {"auto": 0, "prefill": 1, "decode": 2}
+
+MOE_OK = 0
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_status_string(status)} [{status}]: {detail}")
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
+                ("h", ctypes.c_int64), ("top_k", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [("w1q", ctypes.c_void_p), ("w3q", ctypes.c_void_p), ("w2q", ctypes.c_void_p),
+                ("w1s", ctypes.c_void_p), ("w3s", ctypes.c_void_p), ("w2s", ctypes.c_void_p)]
+
+
+class _Shared(ctypes.Structure):
+    _fields_ = [("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m moe_ffn_int4_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_abi_version.restype = ctypes.c_int
+        L.moe_device_check.restype = ctypes.c_int
+        L.moe_quantize_int4.argtypes = [P, i64, i64, i32, P, P, P]
+        L.moe_quantize_int4.restype = ctypes.c_int
+        L.moe_forward_workspace_bytes.argtypes = [ctypes.POINTER(_Dims)]
+        L.moe_forward_workspace_bytes.restype = sz
+        fwd = [ctypes.POINTER(_Dims), P, P, P, ctypes.POINTER(_Experts), ctypes.POINTER(_Shared),
+               P, P, P]
+        L.moe_forward.argtypes = fwd + [P, sz, P]
+        L.moe_forward.restype = ctypes.c_int
+        L.moe_forward_path.argtypes = fwd + [i32, P, sz, P]
+        L.moe_forward_path.restype = ctypes.c_int
+        L.moe_route_workspace_bytes.argtypes = [ctypes.POINTER(_Dims)]
+        L.moe_route_workspace_bytes.restype = sz
+        L.moe_route.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.moe_route.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        raise MoEError(status, lib().moe_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dims(T, d, E, h, top_k) -> _Dims:
+    return _Dims(int(T), int(d), int(E), int(h), int(top_k), GROUP)
+
+
+# --------------------------------------------------------------- quantizer
+
+def quantize_int4(w: torch.Tensor, q: Optional[torch.Tensor] = None,
+                  scales: Optional[torch.Tensor] = None):
+    """Int4 group quantizer: fp32 [rows, K] -> (uint8 [rows, K/2], fp32 [rows, K/128]).
+
+    ``w`` may have leading batch dims; they are flattened into rows.
+    """
+    _need(w, "w", torch.float32)
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    if q is None:
+        q = torch.empty(w.shape[:-1] + (K // 2,), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(w.shape[:-1] + (K // GROUP,), dtype=torch.float32, device=w.device)
+    _need(q, "q", torch.uint8)
+    _need(scales, "scales", torch.float32)
+    if q.numel() != rows * (K // 2) or scales.numel() != rows * (K // GROUP):
+        raise ValueError("q / scales have the wrong number of elements")
+    _check(lib().moe_quantize_int4(_ptr(w), rows, K, GROUP, _ptr(q), _ptr(scales),
+                                   _stream(w.device)))
+    return q, scales
+
+
+@dataclass
+class Int4Experts:
+    """Stacked routed experts in the library's int4 layout."""
+
+    w1q: torch.Tensor  # uint8 [E, h, d/2]
+    w3q: torch.Tensor  # uint8 [E, h, d/2]
+    w2q: torch.Tensor  # uint8 [E, d, h/2]
+    w1s: torch.Tensor  # fp32  [E, h, d/128]
+    w3s: torch.Tensor  # fp32  [E, h, d/128]
+    w2s: torch.Tensor  # fp32  [E, d, h/128]
+
+    @property
+    def E(self) -> int:
+        return self.w1q.shape[0]
+
+    @property
+    def h(self) -> int:
+        return self.w1q.shape[1]
+
+    @property
+    def d(self) -> int:
+        return self.w2q.shape[1]
+
+    @staticmethod
+    def empty(E: int, d: int, h: int, device) -> "Int4Experts":
+        u8, f32 = torch.uint8, torch.float32
+        return Int4Experts(
+            torch.empty(E, h, d // 2, dtype=u8, device=device),
+            torch.empty(E, h, d // 2, dtype=u8, device=device),
+            torch.empty(E, d, h // 2, dtype=u8, device=device),
+            torch.empty(E, h, d // GROUP, dtype=f32, device=device),
+            torch.empty(E, h, d // GROUP, dtype=f32, device=device),
+            torch.empty(E, d, h // GROUP, dtype=f32, device=device))
+
+    def quantize_expert(self, e: int, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor):
+        """Quantize one expert's fp32 weights (on the GPU) into slot ``e``."""
+        quantize_int4(w1, self.w1q[e], self.w1s[e])
+        quantize_int4(w3, self.w3q[e], self.w3s[e])
+        quantize_int4(w2, self.w2q[e], self.w2s[e])
+
+    def _struct(self) -> _Experts:
+        for name in ("w1q", "w3q", "w2q"):
+            _need(getattr(self, name), name, torch.uint8)
+        for name in ("w1s", "w3s", "w2s"):
+            _need(getattr(self, name), name, torch.float32)
+        return _Experts(*(getattr(self, n).data_ptr() for n in
+                          ("w1q", "w3q", "w2q", "w1s", "w3s", "w2s")))
+
+
+# ----------------------------------------------------------------- forward
+
+def workspace_bytes(T: int, d: int, E: int, h: int, top_k: int) -> int:
+    dims = _dims(T, d, E, h, top_k)
+    n = lib().moe_forward_workspace_bytes(ctypes.byref(dims))
+    if n == 0:
+        raise ValueError(f"invalid layer dims T={T} d={d} E={E} h={h} top_k={top_k}")
+    return n
+
+
+def alloc_workspace(T: int, d: int, E: int, h: int, top_k: int, device) -> torch.Tensor:
+    return torch.empty(workspace_bytes(T, d, E, h, top_k), dtype=torch.uint8, device=device)
+
+
+def forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor],
+            experts: Int4Experts, shared, top_k: int, path: str = "auto",
+            y: Optional[torch.Tensor] = None, topk_ids: Optional[torch.Tensor] = None,
+            topk_gates: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The MoE layer: y bf16 [T, d]. ``shared`` = (S1 [h, d], S3 [h, d], S2 [d, h]) bf16."""
+    _need(x, "x", torch.bfloat16)
+    T, d = x.shape
+    E, h = router_w.shape[0], experts.h
+    _need(router_w, "router_w", torch.float32, (E, d))
+    if router_b is not None:
+        _need(router_b, "router_b", torch.float32, (E,))
+    s1, s3, s2 = shared
+    _need(s1, "S1", torch.bfloat16, (h, d))
+    _need(s3, "S3", torch.bfloat16, (h, d))
+    _need(s2, "S2", torch.bfloat16, (d, h))
+    if experts.E != E or experts.d != d:
+        raise ValueError("experts do not match the router / x")
+    if y is None:
+        y = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16, (T, d))
+    if topk_ids is not None:
+        _need(topk_ids, "topk_ids", torch.int32, (T, top_k))
+    if topk_gates is not None:
+        _need(topk_gates, "topk_gates", torch.float32, (T, top_k))
+    if workspace is None:
+        workspace = alloc_workspace(T, d, E, h, top_k, x.device)
+    dims = _dims(T, d, E, h, top_k)
+    ex = experts._struct()
+    sh = _Shared(s1.data_ptr(), s3.data_ptr(), s2.data_ptr())
+    _check(lib().moe_forward_path(
+        ctypes.byref(dims), _ptr(x), _ptr(router_w), _ptr(router_b), ctypes.byref(ex),
+        ctypes.byref(sh), _ptr(y), _ptr(topk_ids), _ptr(topk_gates), PATHS[path],
+        _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return y
+
+
+def route(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor],
+          top_k: int, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Routing and dispatch alone: ids, gates, logits, counts, offsets, perm, inv."""
+    _need(x, "x", torch.bfloat16)
+    T, d = x.shape
+    E = router_w.shape[0]
+    _need(router_w, "router_w", torch.float32, (E, d))
+    if router_b is not None:
+        _need(router_b, "router_b", torch.float32, (E,))
+    dev = x.device
+    P = T * top_k
+    out = {
+        "ids": torch.empty(T, top_k, dtype=torch.int32, device=dev),
+        "gates": torch.empty(T, top_k, dtype=torch.float32, device=dev),
+        "logits": torch.empty(T, E, dtype=torch.float32, device=dev),
+        "counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "perm": torch.empty(P, dtype=torch.int32, device=dev),
+        "inv": torch.empty(P, dtype=torch.int32, device=dev),
+    }
+    dims = _dims(T, d, E, 128, top_k)
+    if workspace is None:
+        n = lib().moe_route_workspace_bytes(ctypes.byref(dims))
+        if n == 0:
+            raise ValueError(f"invalid routing dims T={T} d={d} E={E} top_k={top_k}")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _check(lib().moe_route(
+        ctypes.byref(dims), _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(out["ids"]),
+        _ptr(out["gates"]), _ptr(out["logits"]), _ptr(out["counts"]), _ptr(out["offsets"]),
+        _ptr(out["perm"]), _ptr(out["inv"]), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
+def unpack_int4(q: torch.Tensor) -> torch.Tensor:
+    """Packed bytes [..., K/2] -> int8 codes [..., K] (low nibble = even index)."""
+    lo = (q.to(torch.int16) & 0xF)
+    hi = (q.to(torch.int16) >> 4) & 0xF
+    codes = torch.stack([lo, hi], dim=-1).reshape(*q.shape[:-1], q.shape[-1] * 2)
+    return torch.where(codes >= 8, codes - 16, codes).to(torch.int8)

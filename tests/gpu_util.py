@@ -1,0 +1,127 @@
+"""Helpers for the GPU parity tests: build a layer on the GPU from the seeded
+workloads, and build the oracle's view of the same layer on the host.
+
+Inputs come only from ``workloads``; the oracle's int4 codes come from the
+oracle's own quantizer applied to the same fp32 draws, never from the GPU.
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+from typing import Dict, Iterable, List, Optional
+
+import numpy as np
+import torch
+
+import moe_ffn_int4_amd as moe
+import workloads as W
+from oracle import native
+from oracle.moe import Int4Expert
+
+TOL = 2e-2  # max relative error of an output row (infinity norm)
+MARGIN = 1e-4  # top-k margin above which expert ids must match exactly
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class Layer:
+    cfg: W.MoEConfig
+    x: torch.Tensor          # bf16 [T, d], CPU
+    wr: torch.Tensor         # fp32 [E, d], CPU
+    b: Optional[torch.Tensor]
+    shared: tuple            # bf16, CPU
+    gen_dev: str             # where routed weights are drawn
+    dev: torch.device
+    x_d: torch.Tensor
+    wr_d: torch.Tensor
+    b_d: Optional[torch.Tensor]
+    shared_d: tuple
+    experts_d: moe.Int4Experts
+
+
+def build_layer(cfg: W.MoEConfig, dev="cuda:0", routed_draw: Optional[str] = None) -> Layer:
+    """The layer on the GPU. Routed weights are drawn on the CPU for small
+    layers and on the GPU (then quantized there) for the 5120 x 8192 ones."""
+    dev = torch.device(dev)
+    if routed_draw is None:
+        routed_draw = "cpu" if cfg.d * cfg.h <= 1 << 22 else str(dev)
+    x = W.gen_x(cfg)
+    wr, b = W.gen_router(cfg)
+    shared = W.gen_shared(cfg)
+    ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev)
+    for e in range(cfg.E):
+        ws = [W.gen_expert_weight(cfg, w, e, routed_draw).to(dev) for w in ("w1", "w3", "w2")]
+        ex.quantize_expert(e, *ws)
+        del ws
+    torch.cuda.synchronize(dev)
+    return Layer(cfg, x, wr, b, shared, routed_draw, dev, x.to(dev), wr.to(dev),
+                 None if b is None else b.to(dev), tuple(s.to(dev) for s in shared), ex)
+
+
+def oracle_expert(layer: Layer, e: int) -> Int4Expert:
+    """Expert e quantized by the oracle from the same fp32 draw."""
+    parts = []
+    for w in ("w1", "w3", "w2"):
+        wf = W.gen_expert_weight(layer.cfg, w, e, layer.gen_dev).cpu().numpy()
+        parts.extend(native.quantize_int4(wf))
+        del wf
+    return Int4Expert(*parts)
+
+
+def oracle_forward_rows(layer: Layer, rows: np.ndarray, gpu_ids: Optional[np.ndarray] = None):
+    """Oracle output for the tokens ``rows`` (per-token C loop).
+
+    Where a token's top-k margin is <= MARGIN, several choices are correct;
+    there the oracle evaluates the layer on the GPU's choice (``gpu_ids``).
+    """
+    from oracle import router_logits, select_topk
+    cfg = layer.cfg
+    xs = layer.x[torch.as_tensor(rows)]
+    b = None if layer.b is None else layer.b.numpy()
+    logits = router_logits(xs, layer.wr.numpy(), b)
+    ids, margin = select_topk(logits, cfg.top_k)
+    forced = None
+    if gpu_ids is not None:
+        tie = margin <= MARGIN
+        if tie.any():
+            forced = ids.copy()
+            forced[tie] = gpu_ids[rows][tie]
+            ids = forced
+    need = sorted(set(int(e) for e in np.unique(ids)))
+    experts: List[Optional[Int4Expert]] = [None] * cfg.E
+    for e in need:
+        experts[e] = oracle_expert(layer, e)
+    r = native.moe_forward_per_token(xs, layer.wr.numpy(), b, cfg.top_k, experts, layer.shared,
+                                     forced_ids=forced)
+    return r, margin
+
+
+def row_errors(y_gpu: torch.Tensor, y_ref: np.ndarray) -> np.ndarray:
+    """Per-row ||y_gpu - y_ref||_inf / max(||y_ref||_inf, 1e-6)."""
+    yg = y_gpu.float().cpu().numpy().astype(np.float64)
+    num = np.abs(yg - y_ref).max(axis=1)
+    den = np.maximum(np.abs(y_ref).max(axis=1), 1e-6)
+    return num / den
+
+
+def check_ids(gpu_ids: np.ndarray, ref_ids: np.ndarray, margin: np.ndarray) -> int:
+    """Ids must match as sets wherever the margin exceeds MARGIN; returns #ties."""
+    sure = margin > MARGIN
+    a = np.sort(gpu_ids[sure], axis=1)
+    b = np.sort(ref_ids[sure], axis=1)
+    bad = np.nonzero(np.any(a != b, axis=1))[0]
+    assert bad.size == 0, f"{bad.size} tokens with a clear margin chose different experts"
+    return int((~sure).sum())
+
+
+def sample_rows(T: int, n: int, seed: int = 0) -> np.ndarray:
+    if n >= T:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(T, size=n, replace=False))
+    rows[0], rows[-1] = 0, T - 1  # the first and the last token always
+    return np.unique(rows)

@@ -1,0 +1,77 @@
+"""K1 quantizer on the GPU vs the oracle: codes and scales bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import moe_ffn_int4_amd as moe
+import workloads as W
+from gpu_util import say
+from oracle import int4_group_quantize
+from oracle import native
+from test_oracle_quantize import _golden_groups, _near_tie_groups
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gpu_quant(w: np.ndarray):
+    q, s = moe.quantize_int4(torch.from_numpy(np.ascontiguousarray(w)).to(DEV))
+    torch.cuda.synchronize()
+    return moe.unpack_int4(q.cpu()).numpy(), s.cpu().numpy()
+
+
+def _assert_same(w, codes, scales):
+    c_ref, s_ref = int4_group_quantize(w)
+    np.testing.assert_array_equal(codes, c_ref)
+    np.testing.assert_array_equal(scales.view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_hand_worked_groups():
+    say("quantize: hand-worked groups")
+    groups = _golden_groups()
+    w = np.stack([g[1] for g in groups])
+    codes, scales = _gpu_quant(w)
+    for i, (name, _, scale_bits, want) in enumerate(groups):
+        assert scales.view(np.uint32)[i, 0] == scale_bits, name
+        np.testing.assert_array_equal(codes[i], want, err_msg=name)
+
+
+def test_near_ties():
+    say("quantize: near ties")
+    w = _near_tie_groups(np.random.default_rng(11))
+    _assert_same(w, *_gpu_quant(w))
+
+
+@pytest.mark.parametrize("rows,K", [(1, 128), (3, 384), (257, 1024), (1000, 5120), (77, 8192)])
+def test_random_shapes(rows, K):
+    say(f"quantize: rows={rows} K={K}")
+    rng = np.random.default_rng(rows * 7 + K)
+    w = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
+    w[:: 5] *= np.float32(2e-5)  # some groups under the 1e-6 clamp
+    if rows > 2:
+        w[1, :128] = 0.0
+    _assert_same(w, *_gpu_quant(w))
+
+
+def test_zero_rows_is_a_no_op():
+    q = torch.full((0, 64), 7, dtype=torch.uint8, device=DEV)
+    s = torch.empty(0, 1, dtype=torch.float32, device=DEV)
+    moe.quantize_int4(torch.empty(0, 128, device=DEV), q, s)
+    torch.cuda.synchronize()
+
+
+def test_rejects_bad_group_multiple():
+    with pytest.raises(moe.MoEError):
+        moe.quantize_int4(torch.zeros(4, 100, device=DEV))
+
+
+def test_full_size_expert_matrix():
+    """One 8192 x 5120 expert matrix drawn on the GPU, checked against the C oracle."""
+    say("quantize: full-size W1 of a 5120 x 8192 expert")
+    cfg = W.config(3)
+    w = W.gen_expert_weight(cfg, "w1", 5, DEV)
+    q, s = moe.quantize_int4(w)
+    torch.cuda.synchronize()
+    c_ref, s_ref = native.quantize_int4(w.cpu().numpy())
+    np.testing.assert_array_equal(moe.unpack_int4(q.cpu()).numpy(), c_ref)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
