@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4 Mixture-of-Experts feed-forward layer on one MI355X.
+
+A step is one full pass of the layer (router, top-k, dispatch, routed + shared
+SwiGLU experts, gate-weighted combine) over one batch of synthetic tokens,
+through the C ABI, with weights already quantized and resident in HBM. The
+default workload is the Scout-shaped decode layer (T=16, d=5120, 16 routed
+experts + 1 shared, h=8192, top-1, int4 g128); ``--config`` picks another of
+the five benchmark layers.
+
+Steps cycle through ``--layers`` independently seeded copies of the layer (as
+consecutive layers of a model would), so a step streams weights that are not
+in the 256 MB last-level cache from the step before.
+
+Prints ONE JSON line: the driver's fields plus
+  roofline      the dominant kernel: algorithmic bytes (or FLOPs) per launch
+                divided by its mean launch time, timed with HIP events recorded
+                by the library around each launch on the caller's stream;
+  cpu_baseline  the CPU oracle (per-token C loop, fp64) timed on the host's
+                cores over a bounded sample of the same workload;
+  detail        per-stage times and whole-step rates.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + TFLOP/s (prefill) and HBM GB/s (decode) on 1 MI355X"
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+DEFAULT_STEPS = {0: 500, 1: 500, 2: 40, 3: 40, 4: 10}
+DEFAULT_WARMUP = {0: 20, 1: 20, 2: 5, 3: 5, 4: 3}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", type=int, default=1, help="benchmark layer 0..4 (default 1)")
+    ap.add_argument("--layers", type=int, default=None, help="independent layer copies to cycle")
+    ap.add_argument("--path", default="auto", choices=["auto", "prefill", "decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+def layer_weight_bytes(cfg) -> int:
+    g = 128
+    routed = cfg.E * 3 * (cfg.h * cfg.d // 2 + cfg.h * (cfg.d // g) * 4)
+    shared = 3 * cfg.h * cfg.d * 2
+    return routed + shared
+
+
+def build_layer(cfg, dev):
+    import torch
+    import moe_ffn_int4_amd as moe
+    import workloads as W
+    x = W.gen_x(cfg)
+    wr, b = W.gen_router(cfg)
+    ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev)
+    for e in range(cfg.E):
+        ws = [W.gen_expert_weight(cfg, w, e, dev) for w in ("w1", "w3", "w2")]
+        ex.quantize_expert(e, *ws)
+        del ws
+    shared_raw = W.gen_shared(cfg, dev)
+    shared = moe.pack_shared(*shared_raw)
+    torch.cuda.synchronize()
+    return dict(cfg=cfg, x=x.to(dev), wr=wr.to(dev), b=None if b is None else b.to(dev),
+                experts=ex, shared=shared, shared_raw=shared_raw, x_cpu=x, wr_cpu=wr, b_cpu=b)
+
+
+def stage_units(cfg, counts):
+    """Algorithmic bytes and FLOPs of each stage for one launch, given the
+    realized per-expert pair counts of the step."""
+    g = 128
+    T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.top_k
+    P = T * k
+    touched = int((counts > 0).sum())
+    w13 = 2 * (h * d // 2 + h * (d // g) * 4)   # one routed expert's W1 + W3 (int4 + scales)
+    w2 = d * h // 2 + d * (h // g) * 4          # its W2
+    up_bytes = touched * w13 + 2 * h * d * 2 + T * d * 2 + (P + T) * h * 2
+    down_bytes = touched * w2 + d * h * 2 + (P + T) * h * 2 + (P + T) * d * 4
+    return {
+        "router": (E * d * 4 + T * d * 2 + T * E * 4, 2.0 * T * d * E),
+        "grouped_up": (up_bytes, 4.0 * (P + T) * d * h),
+        "grouped_down": (down_bytes, 2.0 * (P + T) * d * h),
+        "decode_up": (up_bytes, 4.0 * (P + T) * d * h),
+        "decode_down": (down_bytes + T * d * 2, 2.0 * (P + T) * d * h),
+        "combine": ((P + T) * d * 4 + T * d * 2, 2.0 * P * d),
+        "touched": touched,
+        "step_bytes": touched * (w13 + w2) + 3 * h * d * 2 + E * d * 4 + 2 * T * d * 2,
+    }
+
+
+def cpu_baseline(layer, n_sample, dev):
+    """The CPU oracle on a bounded sample of the workload's tokens."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from oracle import native, router_logits, select_topk
+    from oracle.moe import Int4Expert
+
+    cfg = layer["cfg"]
+    n = min(n_sample, cfg.T)
+    rows = np.linspace(0, cfg.T - 1, n).round().astype(np.int64)
+    xs = layer["x_cpu"][torch.as_tensor(rows)]
+    b = None if layer["b_cpu"] is None else layer["b_cpu"].numpy()
+    ids, _ = select_topk(router_logits(xs, layer["wr_cpu"].numpy(), b), cfg.top_k)
+    experts = [None] * cfg.E
+    for e in sorted(set(ids.ravel().tolist())):  # oracle's own quantization of the same draws
+        parts = []
+        for w in ("w1", "w3", "w2"):
+            parts.extend(native.quantize_int4(W.gen_expert_weight(cfg, w, e, dev).cpu().numpy()))
+        experts[e] = Int4Expert(*parts)
+    shared = tuple(s.cpu() for s in layer["shared_raw"])
+    native.lib()
+    t0 = time.perf_counter()
+    ref = native.moe_forward_per_token(xs, layer["wr_cpu"].numpy(), b, cfg.top_k, experts, shared)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        cores = min(cores, int(os.environ["OMP_NUM_THREADS"]))
+    return ref, rows, {
+        "value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": f"{n} of the {cfg.T} tokens of the first layer copy (fp64 per-token C loop, "
+                  f"{len(set(ids.ravel().tolist()))} experts); {dt:.2f} s wall",
+    }
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one MI355X: this build runs on a single GPU; "
+              "--gpus must be 1 (multi-GPU expert parallelism is design-only here).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import moe_ffn_int4_amd as moe
+    import workloads as W
+
+    if not os.path.exists(moe.LIB_PATH):
+        from moe_ffn_int4_amd import build as _b
+        _b.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if moe.lib().moe_device_check() != 0:
+        raise SystemExit(f"not a gfx950 device: {moe.lib().moe_last_error().decode()}")
+
+    ci = args.config
+    cfg0 = W.config(ci)
+    steps = args.steps if args.steps is not None else DEFAULT_STEPS[ci]
+    warmup = args.warmup if args.warmup is not None else DEFAULT_WARMUP[ci]
+    nlayers = args.layers or max(2, min(8, math.ceil(4e9 / layer_weight_bytes(cfg0))))
+    print(f"[bench] config {ci} {cfg0.name}: T={cfg0.T} d={cfg0.d} E={cfg0.E} h={cfg0.h} "
+          f"k={cfg0.top_k}; {nlayers} layer copies, {warmup} warmup + {steps} timed steps",
+          file=sys.stderr, flush=True)
+
+    layers = [build_layer(cfg0.with_(seed=s), dev) for s in range(nlayers)]
+    ws = moe.alloc_workspace(cfg0.T, cfg0.d, cfg0.E, cfg0.h, cfg0.top_k, dev)
+    y = torch.empty(cfg0.T, cfg0.d, dtype=torch.bfloat16, device=dev)
+    ids = [torch.empty(cfg0.T, cfg0.top_k, dtype=torch.int32, device=dev) for _ in layers]
+
+    def step(i):
+        L = layers[i % nlayers]
+        moe.forward(L["x"], L["wr"], L["b"], L["experts"], L["shared"], cfg0.top_k,
+                    path=args.path, y=y, topk_ids=ids[i % nlayers], workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    counts = [np.bincount(t.cpu().numpy().ravel(), minlength=cfg0.E) for t in ids]
+    print(f"[bench] warmup done; experts touched per layer copy: "
+          f"{[int((c > 0).sum()) for c in counts]}", file=sys.stderr, flush=True)
+
+    moe.profile_enable(True)
+    moe.profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = moe.profile_read()
+    moe.profile_enable(False)
+    wall = t1 - t0
+    ms_per_step = wall * 1e3 / steps
+    value = cfg0.T * steps / wall
+
+    # roofline of the dominant kernel, per launch, averaged over the timed steps
+    units = [stage_units(L["cfg"], c) for L, c in zip(layers, counts)]
+    launched = {k: v for k, v in stages.items() if v[1] > 0}
+    dom = max(launched, key=lambda k: launched[k][0])
+    dom_ms, dom_n = launched[dom]
+    per_step = [u.get(dom, (0, 0.0)) for u in units]
+    # launches of step i use layer copy i % nlayers
+    byts = sum(per_step[i % nlayers][0] for i in range(steps)) / steps
+    flops = sum(per_step[i % nlayers][1] for i in range(steps)) / steps
+    mean_s = dom_ms / dom_n / 1e3
+    decode_like = cfg0.T * cfg0.top_k < 1024
+    if decode_like:
+        achieved = byts / mean_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
+    else:
+        achieved = flops / mean_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None}
+    roof["kernel"] = dom
+    roof["mean_launch_us"] = mean_s * 1e6
+    roof["algorithmic_per_launch"] = byts if decode_like else flops
+
+    step_bytes = sum(units[i % nlayers]["step_bytes"] for i in range(steps)) / steps
+    detail = {
+        "stages_us_per_step": {k: round(v[0] * 1e3 / steps, 2) for k, v in launched.items()},
+        "step_hbm_GBps": step_bytes / (wall / steps) / 1e9,
+        "step_TFLOPs": cfg0.flops() / (wall / steps) / 1e12,
+        "touched_experts": [u["touched"] for u in units],
+        "layer_copies": nlayers,
+        "path": args.path,
+    }
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        detail["copy_calibration_bytes"] = n
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg0.name}: T={cfg0.T} d={cfg0.d} E={cfg0.E}+1 shared "
+                               f"h={cfg0.h} top_k={cfg0.top_k}, int4 g128 routed / bf16 shared",
+                   "T": cfg0.T, "d": cfg0.d, "E": cfg0.E, "h": cfg0.h, "top_k": cfg0.top_k,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        n_sample = args.cpu_sample or (16 if decode_like else 8)
+        ref, rows, base = cpu_baseline(layers[0], n_sample, dev)
+        # spot parity of the same tokens on the GPU (layer copy 0)
+        step(0)
+        torch.cuda.synchronize()
+        yg = y[torch.as_tensor(rows, device=dev)].float().cpu().numpy().astype(np.float64)
+        err = np.abs(yg - ref.y).max(axis=1) / np.maximum(np.abs(ref.y).max(axis=1), 1e-6)
+        base["gpu_vs_oracle_max_row_rel_err"] = float(err.max())
+        out["cpu_baseline"] = base
+    out["detail"] = detail
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -87,6 +87,30 @@ int moe_device_check(void);
 int moe_quantize_int4(const float *w, int64_t rows, int64_t K, int32_t group_size,
                       uint8_t *q, float *scales, void *stream);
 
+/*
+ * The same quantizer writing the tiled layout the forward pass reads
+ * (MI355X-specific storage; codes and scales are bit-identical to
+ * moe_quantize_int4, only their order in memory differs). rows % 16 == 0.
+ * Tile (rb, g) covers rows 16*rb .. 16*rb+15 and reduction columns
+ * 128*g .. 128*g+127; tiles are stored rb-major, t = rb * (K/128) + g:
+ *   q       byte  t*1024 + (row % 16)*64 + (k % 128)/2   (low nibble = even k)
+ *   scales  float t*16 + (row % 16)
+ * A wavefront reads one 1 KB tile (and its 64 B of scales) per access.
+ */
+int moe_quantize_int4_tiled(const float *w, int64_t rows, int64_t K, int32_t group_size,
+                            uint8_t *q, float *scales, void *stream);
+
+/*
+ * Repack a bf16 matrix [rows, K] (rows % 16 == 0, K % 128 == 0) into the
+ * tiled order the forward pass reads for the shared expert: tile
+ * t = (row/16) * (K/128) + k/128 holds 16 rows x 128 columns as 4 steps of
+ * 32 columns, element (row, k) at
+ *   t*2048 + ((k % 128)/32)*512 + (row % 16)*32 + (k % 32).
+ * src and dst are device buffers of rows*K bf16 and must not overlap.
+ */
+int moe_pack_bf16_tiled(const uint16_t *src, int64_t rows, int64_t K, uint16_t *dst,
+                        void *stream);
+
 typedef struct moe_dims {
     int64_t T;      /* tokens, >= 1 */
     int64_t d;      /* model dim, multiple of 128 */
@@ -96,15 +120,17 @@ typedef struct moe_dims {
     int32_t group_size; /* must be MOE_GROUP_SIZE */
 } moe_dims;
 
-/* Routed experts in the layout moe_quantize_int4 writes, experts stacked:
- *   w1q, w3q [E, h, d/2] bytes   w1s, w3s [E, h, d/128] fp32
- *   w2q      [E, d, h/2] bytes   w2s      [E, d, h/128] fp32 */
+/* Routed experts, each matrix written by moe_quantize_int4_tiled, experts
+ * stacked (expert e's matrix starts at e times the matrix size):
+ *   w1q, w3q [E] x tiled [h, d]: E*h*d/2 bytes   w1s, w3s: E*h*d/128 fp32
+ *   w2q      [E] x tiled [d, h]: E*d*h/2 bytes   w2s:      E*d*h/128 fp32 */
 typedef struct moe_experts_int4 {
     const uint8_t *w1q, *w3q, *w2q;
     const float *w1s, *w3s, *w2s;
 } moe_experts_int4;
 
-/* Shared expert, bf16: s1, s3 [h, d]; s2 [d, h]. */
+/* Shared expert, bf16, each matrix packed by moe_pack_bf16_tiled:
+ * s1, s3 from [h, d]; s2 from [d, h]. */
 typedef struct moe_shared_bf16 {
     const uint16_t *s1, *s3, *s2;
 } moe_shared_bf16;
@@ -164,6 +190,31 @@ int moe_route(const moe_dims *dims, const uint16_t *x, const float *router_w,
               const float *router_b, int32_t *topk_ids, float *topk_gates,
               float *logits, int32_t *counts, int32_t *offsets, int32_t *perm,
               int32_t *inv, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Per-stage timing for benchmarks (not part of the layer's arithmetic).
+ * While enabled, every moe_forward / moe_route call records a hipEvent on its
+ * stream before and after each kernel launch. moe_profile_read waits for the
+ * recorded events, writes the summed duration in milliseconds and the launch
+ * count of each stage (arrays of `n` entries, n <= MOE_STAGE_COUNT), and
+ * resets the sums. Enabling adds one event record per launch; it is off by
+ * default. State is process-wide; it is not meant for concurrent callers.
+ */
+enum moe_stage {
+    MOE_STAGE_ROUTER = 0,      /* K2 router logits */
+    MOE_STAGE_TOPK = 1,        /* K2 top-k + gates */
+    MOE_STAGE_DISPATCH = 2,    /* K3 */
+    MOE_STAGE_UP = 3,          /* K4 + shared up-projection, SwiGLU */
+    MOE_STAGE_DOWN = 4,        /* K5 + shared down-projection */
+    MOE_STAGE_COMBINE = 5,     /* gate-weighted sum + shared, bf16 out */
+    MOE_STAGE_DECODE_UP = 6,   /* decode path: streaming up-projection */
+    MOE_STAGE_DECODE_DOWN = 7, /* decode path: streaming down-projection + combine */
+    MOE_STAGE_COUNT = 8
+};
+
+int moe_profile_enable(int on);
+int moe_profile_read(double *ms, int64_t *launches, int n);
+const char *moe_stage_name(int stage);
 
 #ifdef __cplusplus
 }

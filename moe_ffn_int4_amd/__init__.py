@@ -7,8 +7,14 @@ HIP kernels. There is no fallback: if the library is missing, importing the
 functions below raises.
 
     q, s = quantize_int4(w_fp32_cuda)                 # int4 group quantizer
+    experts = Int4Experts.empty(E, d, h, dev)         # routed experts, tiled int4
+    experts.quantize_expert(e, w1, w3, w2)            #   (fp32 weights on the GPU)
+    shared = pack_shared(s1, s3, s2)                  # shared expert, tiled bf16
     y = forward(x, router_w, router_b, experts, shared, top_k)
     r = route(x, router_w, router_b, top_k)           # routing/dispatch only
+
+Weights live in the tiled layouts the kernels read (see include/moe_int4.h);
+untile_int4 / untile_scales / untile_bf16 convert them back to row-major.
 """
 from __future__ import annotations
 
@@ -67,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.moe_device_check.restype = ctypes.c_int
         L.moe_quantize_int4.argtypes = [P, i64, i64, i32, P, P, P]
         L.moe_quantize_int4.restype = ctypes.c_int
+        L.moe_quantize_int4_tiled.argtypes = [P, i64, i64, i32, P, P, P]
+        L.moe_quantize_int4_tiled.restype = ctypes.c_int
+        L.moe_pack_bf16_tiled.argtypes = [P, i64, i64, P, P]
+        L.moe_pack_bf16_tiled.restype = ctypes.c_int
         L.moe_forward_workspace_bytes.argtypes = [ctypes.POINTER(_Dims)]
         L.moe_forward_workspace_bytes.restype = sz
         fwd = [ctypes.POINTER(_Dims), P, P, P, ctypes.POINTER(_Experts), ctypes.POINTER(_Shared),
@@ -79,6 +89,12 @@ def lib() -> ctypes.CDLL:
         L.moe_route_workspace_bytes.restype = sz
         L.moe_route.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.moe_route.restype = ctypes.c_int
+        L.moe_profile_enable.argtypes = [ctypes.c_int]
+        L.moe_profile_enable.restype = ctypes.c_int
+        L.moe_profile_read.argtypes = [P, P, ctypes.c_int]
+        L.moe_profile_read.restype = ctypes.c_int
+        L.moe_stage_name.argtypes = [ctypes.c_int]
+        L.moe_stage_name.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -120,10 +136,12 @@ def _dims(T, d, E, h, top_k) -> _Dims:
 # --------------------------------------------------------------- quantizer
 
 def quantize_int4(w: torch.Tensor, q: Optional[torch.Tensor] = None,
-                  scales: Optional[torch.Tensor] = None):
+                  scales: Optional[torch.Tensor] = None, tiled: bool = False):
     """Int4 group quantizer: fp32 [rows, K] -> (uint8 [rows, K/2], fp32 [rows, K/128]).
 
-    ``w`` may have leading batch dims; they are flattened into rows.
+    ``w`` may have leading batch dims; they are flattened into rows. With
+    ``tiled`` the outputs hold the same codes and scales in the 16-row tile
+    order the forward pass reads (rows must be a multiple of 16).
     """
     _need(w, "w", torch.float32)
     K = w.shape[-1]
@@ -136,9 +154,27 @@ def quantize_int4(w: torch.Tensor, q: Optional[torch.Tensor] = None,
     _need(scales, "scales", torch.float32)
     if q.numel() != rows * (K // 2) or scales.numel() != rows * (K // GROUP):
         raise ValueError("q / scales have the wrong number of elements")
-    _check(lib().moe_quantize_int4(_ptr(w), rows, K, GROUP, _ptr(q), _ptr(scales),
-                                   _stream(w.device)))
+    fn = lib().moe_quantize_int4_tiled if tiled else lib().moe_quantize_int4
+    _check(fn(_ptr(w), rows, K, GROUP, _ptr(q), _ptr(scales), _stream(w.device)))
     return q, scales
+
+
+def pack_bf16_tiled(src: torch.Tensor, dst: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [rows, K] -> the tiled order the forward pass reads (same shape)."""
+    _need(src, "src", torch.bfloat16)
+    if src.dim() != 2:
+        raise ValueError("src must be 2-D")
+    rows, K = src.shape
+    if dst is None:
+        dst = torch.empty_like(src)
+    _need(dst, "dst", torch.bfloat16, (rows, K))
+    _check(lib().moe_pack_bf16_tiled(_ptr(src), rows, K, _ptr(dst), _stream(src.device)))
+    return dst
+
+
+def pack_shared(s1: torch.Tensor, s3: torch.Tensor, s2: torch.Tensor):
+    """The shared expert's bf16 weights (S1, S3 [h, d], S2 [d, h]) in tiled order."""
+    return tuple(pack_bf16_tiled(s) for s in (s1, s3, s2))
 
 
 @dataclass
@@ -176,10 +212,10 @@ class Int4Experts:
             torch.empty(E, d, h // GROUP, dtype=f32, device=device))
 
     def quantize_expert(self, e: int, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor):
-        """Quantize one expert's fp32 weights (on the GPU) into slot ``e``."""
-        quantize_int4(w1, self.w1q[e], self.w1s[e])
-        quantize_int4(w3, self.w3q[e], self.w3s[e])
-        quantize_int4(w2, self.w2q[e], self.w2s[e])
+        """Quantize one expert's fp32 weights (on the GPU) into slot ``e`` (tiled)."""
+        quantize_int4(w1, self.w1q[e], self.w1s[e], tiled=True)
+        quantize_int4(w3, self.w3q[e], self.w3s[e], tiled=True)
+        quantize_int4(w2, self.w2q[e], self.w2s[e], tiled=True)
 
     def _struct(self) -> _Experts:
         for name in ("w1q", "w3q", "w2q"):
@@ -274,9 +310,42 @@ def route(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tens
     return out
 
 
+def untile_int4(q: torch.Tensor, rows: int, K: int) -> torch.Tensor:
+    """Tiled int4 bytes of one [rows, K] matrix -> row-major bytes [rows, K/2]."""
+    return q.reshape(rows // 16, K // GROUP, 16, GROUP // 2).permute(0, 2, 1, 3).reshape(rows, K // 2)
+
+
+def untile_scales(s: torch.Tensor, rows: int, K: int) -> torch.Tensor:
+    """Tiled scales of one [rows, K] matrix -> row-major [rows, K/128]."""
+    return s.reshape(rows // 16, K // GROUP, 16).permute(0, 2, 1).reshape(rows, K // GROUP)
+
+
+def untile_bf16(t: torch.Tensor, rows: int, K: int) -> torch.Tensor:
+    """Tiled bf16 [rows, K] (pack_bf16_tiled order) -> row-major [rows, K]."""
+    return t.reshape(rows // 16, K // GROUP, 4, 16, 32).permute(0, 3, 1, 2, 4).reshape(rows, K)
+
+
 def unpack_int4(q: torch.Tensor) -> torch.Tensor:
     """Packed bytes [..., K/2] -> int8 codes [..., K] (low nibble = even index)."""
     lo = (q.to(torch.int16) & 0xF)
     hi = (q.to(torch.int16) >> 4) & 0xF
     codes = torch.stack([lo, hi], dim=-1).reshape(*q.shape[:-1], q.shape[-1] * 2)
     return torch.where(codes >= 8, codes - 16, codes).to(torch.int8)
+
+
+# ------------------------------------------------------------------ timing
+
+STAGE_COUNT = 8
+
+
+def profile_enable(on: bool = True) -> None:
+    """Record a HIP event around every kernel launch of later calls."""
+    _check(lib().moe_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """{stage name: (summed ms, launches)} since the last read; resets the sums."""
+    ms = (ctypes.c_double * STAGE_COUNT)()
+    n = (ctypes.c_int64 * STAGE_COUNT)()
+    _check(lib().moe_profile_read(ms, n, STAGE_COUNT))
+    return {lib().moe_stage_name(i).decode(): (ms[i], n[i]) for i in range(STAGE_COUNT)}

@@ -12,6 +12,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "kernels.h"
 
@@ -44,18 +45,31 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace sections (byte offsets from the workspace base).
 struct Layout {
-    size_t logits, ids, gates, counts, offsets, tile_base, perm, inv, routing_end, H, O, total;
+    size_t partials, logits, ids, gates, counts, offsets, tile_base, perm, inv, chunks, nchunks,
+        routing_end, x_perm, H, O, total;
+    int slices;
+    int max_chunks;
 };
+
+int64_t max_decode_chunks(const moe_dims& d) {
+    const int64_t P = d.T * d.top_k;
+    const int64_t R = moe::kDecodeRows;
+    return (d.E < P ? d.E : P) + (P + R - 1) / R + (d.T + R - 1) / R;
+}
 
 Layout layout(const moe_dims& d) {
     const size_t T = d.T, E = d.E, P = static_cast<size_t>(d.T) * d.top_k;
     Layout L{};
+    const moe::RouterPlan plan = moe::router_plan(d.T, d.d, d.E);
+    L.slices = plan.slices;
+    L.max_chunks = static_cast<int>(max_decode_chunks(d));
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
         off += round_up(bytes);
         return at;
     };
+    L.partials = take(static_cast<size_t>(plan.slices) * T * E * 4);
     L.logits = take(T * E * 4);
     L.ids = take(P * 4);
     L.gates = take(P * 4);
@@ -64,12 +78,23 @@ Layout layout(const moe_dims& d) {
     L.tile_base = take((E + 2) * 4);
     L.perm = take(P * 4);
     L.inv = take(P * 4);
+    L.chunks = take(static_cast<size_t>(L.max_chunks) * 16);
+    L.nchunks = take(4);
     L.routing_end = off;
+    L.x_perm = take(T * static_cast<size_t>(d.d) * 2);
     L.H = take((P + T) * static_cast<size_t>(d.h) * 2);
     L.O = take((P + T) * static_cast<size_t>(d.d) * 4);
     L.total = off;
     return L;
 }
+
+// The one-block routing kernel covers small batches (decode).
+bool small_routing(const moe_dims& d) {
+    return d.T * d.E <= moe::kSmallRouteLogits && d.T * d.top_k <= moe::kSmallRoutePairs;
+}
+
+// MOE_PATH_AUTO: the streaming decode path for small batches.
+constexpr int64_t kDecodeMaxPairs = 64;
 
 int check_dims(const moe_dims* d) {
     if (!d) return fail(MOE_ERR_INVALID_ARG, "dims is NULL");
@@ -111,6 +136,54 @@ int check_ptr(const void* p, const char* name, size_t align = 16) {
         if (e_ != hipSuccess) return hip_fail(e_, what); \
     } while (0)
 
+// ---- optional per-stage timing (moe_profile_*)
+struct Prof {
+    std::mutex mu;
+    bool on = false;
+    struct Rec {
+        int stage;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> pending;
+    std::vector<hipEvent_t> pool;
+    double ms[MOE_STAGE_COUNT] = {};
+    int64_t n[MOE_STAGE_COUNT] = {};
+};
+Prof& prof() {
+    static Prof p;
+    return p;
+}
+
+hipError_t prof_event(hipEvent_t* ev) {
+    Prof& P = prof();
+    if (!P.pool.empty()) {
+        *ev = P.pool.back();
+        P.pool.pop_back();
+        return hipSuccess;
+    }
+    return hipEventCreate(ev);
+}
+
+// Launch `fn` (returning hipError_t) as `stage`, bracketed by events when enabled.
+template <typename F>
+int timed(int stage, hipStream_t s, const char* what, F&& fn) {
+    Prof& P = prof();
+    std::unique_lock<std::mutex> lock(P.mu);
+    if (!P.on) {
+        lock.unlock();
+        HIP_CHECK(fn(), what);
+        return MOE_OK;
+    }
+    Prof::Rec r{stage, nullptr, nullptr};
+    HIP_CHECK(prof_event(&r.a), "hipEventCreate");
+    HIP_CHECK(prof_event(&r.b), "hipEventCreate");
+    HIP_CHECK(hipEventRecord(r.a, s), "hipEventRecord");
+    HIP_CHECK(fn(), what);
+    HIP_CHECK(hipEventRecord(r.b, s), "hipEventRecord");
+    P.pending.push_back(r);
+    return MOE_OK;
+}
+
 // Cached "is gfx950" per device ordinal.
 int device_ok() {
     static std::mutex mu;
@@ -151,6 +224,7 @@ int check_forward_args(const moe_dims* dims, const uint16_t* x, const float* rou
 }
 
 struct Routing {
+    float* partials;
     float* logits;
     int32_t* ids;
     float* gates;
@@ -159,25 +233,54 @@ struct Routing {
     int32_t* tile_base;
     int32_t* perm;
     int32_t* inv;
+    int4* chunks;
+    int32_t* nchunks;
 };
 
 Routing carve(const moe_dims& d, void* ws) {
     const Layout L = layout(d);
     char* b = static_cast<char*>(ws);
-    return Routing{reinterpret_cast<float*>(b + L.logits),   reinterpret_cast<int32_t*>(b + L.ids),
-                   reinterpret_cast<float*>(b + L.gates),    reinterpret_cast<int32_t*>(b + L.counts),
-                   reinterpret_cast<int32_t*>(b + L.offsets), reinterpret_cast<int32_t*>(b + L.tile_base),
-                   reinterpret_cast<int32_t*>(b + L.perm),   reinterpret_cast<int32_t*>(b + L.inv)};
+    Routing R;
+    R.partials = reinterpret_cast<float*>(b + L.partials);
+    R.logits = reinterpret_cast<float*>(b + L.logits);
+    R.ids = reinterpret_cast<int32_t*>(b + L.ids);
+    R.gates = reinterpret_cast<float*>(b + L.gates);
+    R.counts = reinterpret_cast<int32_t*>(b + L.counts);
+    R.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+    R.tile_base = reinterpret_cast<int32_t*>(b + L.tile_base);
+    R.perm = reinterpret_cast<int32_t*>(b + L.perm);
+    R.inv = reinterpret_cast<int32_t*>(b + L.inv);
+    R.chunks = reinterpret_cast<int4*>(b + L.chunks);
+    R.nchunks = reinterpret_cast<int32_t*>(b + L.nchunks);
+    return R;
 }
 
+// Router partial logits, then either the one-block small-batch finish (top-k,
+// dispatch, decode chunks) or the top-k kernel + the per-expert dispatch kernel.
 int run_routing(const moe_dims& d, const uint16_t* x, const float* wr, const float* b,
-                const Routing& R, int32_t* ids_out, float* gates_out, hipStream_t s) {
-    HIP_CHECK(moe::launch_router_logits(x, wr, b, d.T, d.d, d.E, R.logits, s), "router launch");
-    HIP_CHECK(moe::launch_topk(R.logits, d.T, d.E, d.top_k, R.ids, R.gates, ids_out, gates_out, s),
-              "top-k launch");
-    HIP_CHECK(moe::launch_dispatch(R.ids, d.T, d.top_k, d.E, moe::kPrefillBM, R.counts, R.offsets,
-                                   R.tile_base, R.perm, R.inv, s),
-              "dispatch launch");
+                const Routing& R, int32_t* ids_out, float* gates_out, uint16_t* x_perm,
+                hipStream_t s) {
+    const moe::RouterPlan plan = moe::router_plan(d.T, d.d, d.E);
+    CHECK(timed(MOE_STAGE_ROUTER, s, "router launch", [&] {
+        return moe::launch_router_partials(x, wr, d.T, d.d, d.E, plan, R.partials, x_perm, s);
+    }));
+    if (small_routing(d)) {
+        CHECK(timed(MOE_STAGE_TOPK, s, "small routing launch", [&] {
+            return moe::launch_route_small(R.partials, plan.slices, b, d.T, d.E, d.top_k,
+                                           moe::kPrefillBM, R.logits, R.ids, R.gates, ids_out,
+                                           gates_out, R.counts, R.offsets, R.tile_base, R.perm,
+                                           R.inv, R.chunks, R.nchunks, s);
+        }));
+        return MOE_OK;
+    }
+    CHECK(timed(MOE_STAGE_TOPK, s, "top-k launch", [&] {
+        return moe::launch_topk(R.partials, plan.slices, b, d.T, d.E, d.top_k, R.logits, R.ids,
+                                R.gates, ids_out, gates_out, s);
+    }));
+    CHECK(timed(MOE_STAGE_DISPATCH, s, "dispatch launch", [&] {
+        return moe::launch_dispatch(R.ids, d.T, d.top_k, d.E, moe::kPrefillBM, R.counts, R.offsets,
+                                    R.tile_base, R.perm, R.inv, R.chunks, R.nchunks, s);
+    }));
     return MOE_OK;
 }
 
@@ -202,8 +305,8 @@ int moe_abi_version(void) { return MOE_INT4_ABI_VERSION; }
 
 int moe_device_check(void) { return device_ok(); }
 
-int moe_quantize_int4(const float* w, int64_t rows, int64_t K, int32_t group_size, uint8_t* q,
-                      float* scales, void* stream) {
+static int quantize(const float* w, int64_t rows, int64_t K, int32_t group_size, uint8_t* q,
+                    float* scales, bool tiled, void* stream) {
     g_last_error.clear();
     if (group_size != MOE_GROUP_SIZE)
         return fail(MOE_ERR_INVALID_ARG, "group_size %d unsupported (only %d)", group_size,
@@ -212,13 +315,44 @@ int moe_quantize_int4(const float* w, int64_t rows, int64_t K, int32_t group_siz
     if (K < group_size || K % group_size)
         return fail(MOE_ERR_INVALID_ARG, "K = %lld must be a positive multiple of %d", (long long)K,
                     group_size);
+    if (tiled && rows % 16)
+        return fail(MOE_ERR_INVALID_ARG, "rows = %lld must be a multiple of 16 for the tiled layout",
+                    (long long)rows);
     if (rows == 0) return MOE_OK;
     CHECK(check_ptr(w, "w"));
-    CHECK(check_ptr(q, "q", 2));
+    CHECK(check_ptr(q, "q", tiled ? 16 : 2));
     CHECK(check_ptr(scales, "scales", 4));
     CHECK(device_ok());
-    HIP_CHECK(moe::launch_quantize_int4(w, rows, K, q, scales, static_cast<hipStream_t>(stream)),
+    HIP_CHECK(moe::launch_quantize_int4(w, rows, K, q, scales, tiled, static_cast<hipStream_t>(stream)),
               "quantize launch");
+    return MOE_OK;
+}
+
+int moe_quantize_int4(const float* w, int64_t rows, int64_t K, int32_t group_size, uint8_t* q,
+                      float* scales, void* stream) {
+    return quantize(w, rows, K, group_size, q, scales, false, stream);
+}
+
+int moe_quantize_int4_tiled(const float* w, int64_t rows, int64_t K, int32_t group_size, uint8_t* q,
+                            float* scales, void* stream) {
+    return quantize(w, rows, K, group_size, q, scales, true, stream);
+}
+
+int moe_pack_bf16_tiled(const uint16_t* src, int64_t rows, int64_t K, uint16_t* dst, void* stream) {
+    g_last_error.clear();
+    if (rows < 0 || rows % 16)
+        return fail(MOE_ERR_INVALID_ARG, "rows = %lld must be a non-negative multiple of 16",
+                    (long long)rows);
+    if (K < 128 || K % 128)
+        return fail(MOE_ERR_INVALID_ARG, "K = %lld must be a positive multiple of 128", (long long)K);
+    if (rows == 0) return MOE_OK;
+    CHECK(check_ptr(src, "src"));
+    CHECK(check_ptr(dst, "dst"));
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t n = static_cast<uintptr_t>(rows) * K * 2;
+    if (a < b + n && b < a + n) return fail(MOE_ERR_INVALID_ARG, "src and dst overlap");
+    CHECK(device_ok());
+    HIP_CHECK(moe::launch_pack_bf16(src, rows, K, dst, static_cast<hipStream_t>(stream)), "pack launch");
     return MOE_OK;
 }
 
@@ -251,7 +385,7 @@ int moe_route(const moe_dims* dims, const uint16_t* x, const float* router_w,
     const moe_dims& d = *dims;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Routing R = carve(d, workspace);
-    CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates, s));
+    CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates, nullptr, s));
     const size_t P = static_cast<size_t>(d.T) * d.top_k;
     if (logits)
         HIP_CHECK(hipMemcpyAsync(logits, R.logits, d.T * d.E * 4, hipMemcpyDeviceToDevice, s), "copy");
@@ -296,44 +430,88 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
     float* O = reinterpret_cast<float*>(base + L.O);
     const int64_t P = d.T * d.top_k;
 
-    CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates, s));
+    const bool decode =
+        path == MOE_PATH_DECODE || (path == MOE_PATH_AUTO && P <= kDecodeMaxPairs);
+    uint16_t* x_perm = reinterpret_cast<uint16_t*>(base + L.x_perm);
+    CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates, decode ? x_perm : nullptr, s));
 
-    moe::GroupedGemmArgs g{};
-    g.T = d.T;
-    g.P = P;
-    g.top_k = d.top_k;
-    g.E = static_cast<int>(d.E);
-    g.perm = R.perm;
-    g.offsets = R.offsets;
-    g.counts = R.counts;
-    g.tile_base = R.tile_base;
+    if (decode) {
+        moe::DecodeArgs a{};
+        a.T = d.T;
+        a.P = P;
+        a.top_k = d.top_k;
+        a.E = static_cast<int>(d.E);
+        a.perm = R.perm;
+        a.chunks = R.chunks;
+        a.nchunks = R.nchunks;
+        a.a = x;
+        a.a_perm = x_perm;
+        a.K = d.d;
+        a.N = d.h;
+        a.wq0 = ex->w1q;
+        a.ws0 = ex->w1s;
+        a.wq1 = ex->w3q;
+        a.ws1 = ex->w3s;
+        a.sh0 = sh->s1;
+        a.sh1 = sh->s3;
+        a.h_out = H;
+        CHECK(timed(MOE_STAGE_DECODE_UP, s, "decode up launch",
+                    [&] { return moe::launch_decode_up(a, L.max_chunks, s); }));
+        a.a = H;
+        a.a_perm = H;  // routed rows of H were written interleaved by the up projection
+        a.K = d.h;
+        a.N = d.d;
+        a.wq0 = ex->w2q;
+        a.ws0 = ex->w2s;
+        a.wq1 = nullptr;
+        a.ws1 = nullptr;
+        a.sh0 = sh->s2;
+        a.sh1 = nullptr;
+        a.h_out = nullptr;
+        a.o_out = O;
+        CHECK(timed(MOE_STAGE_DECODE_DOWN, s, "decode down launch",
+                    [&] { return moe::launch_decode_down(a, L.max_chunks, s); }));
+    } else {
+        moe::GroupedGemmArgs g{};
+        g.T = d.T;
+        g.P = P;
+        g.top_k = d.top_k;
+        g.E = static_cast<int>(d.E);
+        g.perm = R.perm;
+        g.offsets = R.offsets;
+        g.counts = R.counts;
+        g.tile_base = R.tile_base;
 
-    g.a = x;
-    g.K = d.d;
-    g.N = d.h;
-    g.wq0 = ex->w1q;
-    g.ws0 = ex->w1s;
-    g.wq1 = ex->w3q;
-    g.ws1 = ex->w3s;
-    g.sh0 = sh->s1;
-    g.sh1 = sh->s3;
-    g.h_out = H;
-    HIP_CHECK(moe::launch_grouped_up(g, s), "grouped up launch");
+        g.a = x;
+        g.K = d.d;
+        g.N = d.h;
+        g.wq0 = ex->w1q;
+        g.ws0 = ex->w1s;
+        g.wq1 = ex->w3q;
+        g.ws1 = ex->w3s;
+        g.sh0 = sh->s1;
+        g.sh1 = sh->s3;
+        g.h_out = H;
+        CHECK(timed(MOE_STAGE_UP, s, "grouped up launch", [&] { return moe::launch_grouped_up(g, s); }));
 
-    g.a = H;
-    g.K = d.h;
-    g.N = d.d;
-    g.wq0 = ex->w2q;
-    g.ws0 = ex->w2s;
-    g.wq1 = nullptr;
-    g.ws1 = nullptr;
-    g.sh0 = sh->s2;
-    g.sh1 = nullptr;
-    g.h_out = nullptr;
-    g.o_out = O;
-    HIP_CHECK(moe::launch_grouped_down(g, s), "grouped down launch");
+        g.a = H;
+        g.K = d.h;
+        g.N = d.d;
+        g.wq0 = ex->w2q;
+        g.ws0 = ex->w2s;
+        g.wq1 = nullptr;
+        g.ws1 = nullptr;
+        g.sh0 = sh->s2;
+        g.sh1 = nullptr;
+        g.h_out = nullptr;
+        g.o_out = O;
+        CHECK(timed(MOE_STAGE_DOWN, s, "grouped down launch",
+                    [&] { return moe::launch_grouped_down(g, s); }));
+    }
 
-    HIP_CHECK(moe::launch_combine(O, R.gates, R.inv, d.T, P, d.top_k, d.d, y, s), "combine launch");
+    CHECK(timed(MOE_STAGE_COMBINE, s, "combine launch", [&] {
+        return moe::launch_combine(O, R.gates, R.inv, d.T, P, d.top_k, d.d, y, s);
+    }));
     return MOE_OK;
 }
 
@@ -343,6 +521,45 @@ int moe_forward(const moe_dims* dims, const uint16_t* x, const float* router_w,
                 void* workspace, size_t workspace_bytes, void* stream) {
     return moe_forward_path(dims, x, router_w, router_b, experts, shared, y, topk_ids, topk_gates,
                             MOE_PATH_AUTO, workspace, workspace_bytes, stream);
+}
+
+int moe_profile_enable(int on) {
+    Prof& P = prof();
+    std::lock_guard<std::mutex> lock(P.mu);
+    P.on = on != 0;
+    return MOE_OK;
+}
+
+int moe_profile_read(double* ms, int64_t* launches, int n) {
+    g_last_error.clear();
+    if (n < 0 || n > MOE_STAGE_COUNT) return fail(MOE_ERR_INVALID_ARG, "n = %d outside [0, %d]", n, MOE_STAGE_COUNT);
+    Prof& P = prof();
+    std::lock_guard<std::mutex> lock(P.mu);
+    for (const Prof::Rec& r : P.pending) {
+        HIP_CHECK(hipEventSynchronize(r.b), "hipEventSynchronize");
+        float t = 0.f;
+        HIP_CHECK(hipEventElapsedTime(&t, r.a, r.b), "hipEventElapsedTime");
+        P.ms[r.stage] += t;
+        P.n[r.stage] += 1;
+        P.pool.push_back(r.a);
+        P.pool.push_back(r.b);
+    }
+    P.pending.clear();
+    for (int i = 0; i < n; ++i) {
+        if (ms) ms[i] = P.ms[i];
+        if (launches) launches[i] = P.n[i];
+    }
+    for (int i = 0; i < MOE_STAGE_COUNT; ++i) {
+        P.ms[i] = 0.0;
+        P.n[i] = 0;
+    }
+    return MOE_OK;
+}
+
+const char* moe_stage_name(int stage) {
+    static const char* names[MOE_STAGE_COUNT] = {"router", "topk", "dispatch", "grouped_up",
+                                                 "grouped_down", "combine", "decode_up", "decode_down"};
+    return (stage >= 0 && stage < MOE_STAGE_COUNT) ? names[stage] : "unknown";
 }
 
 }  // extern "C"

@@ -1,0 +1,246 @@
+// decode.hip -- K7: HBM-streaming expert FFN for small batches (gfx950).
+//
+// In generation each step brings one new token per sequence (lshu.cn page,
+// section "数据流"), so a decode batch is a handful of tokens: every touched
+// expert's weights are streamed from HBM once and used for only its few
+// tokens. This path reads each weight byte exactly once and is bound by HBM
+// bandwidth.
+//
+// Work: row chunks (<= 16 token rows of one group: the shared expert first,
+// the largest work item, then routed experts in id order) from the routing
+// step, times blocks of 64 output features. A 256-thread block is 4 waves;
+// each wave owns 16 output features and streams them over the whole reduction
+// dimension on its own (no LDS, no block barriers), keeping the next groups'
+// loads in flight in a register ring. v_mfma_f32_16x16x32_bf16 takes the
+// chunk's tokens as its 16 rows (absent rows are zero) and the features as
+// its 16 columns.
+//
+// Weights come in the tiled layouts of moe_quantize_int4_tiled /
+// moe_pack_bf16_tiled, so every weight access of a wave is one contiguous
+// 1 KB tile (plus 64 B of scales), read with non-temporal loads.
+// Int4 weights (routed experts): per 128-wide group a lane streams one 16-byte
+// piece (32 codes) of its feature's row. Codes become bf16 (128 + u),
+// u = code + 8, by OR-ing offset-binary nibbles into the bit pattern of 128.0
+// (about one VALU op per code; gfx950 has no packed bf16 add to remove the
+// offset). The offset is removed exactly by one extra MFMA per 32-wide step
+// against a constant B of -136 (shared by W1 and W3): a group's accumulator
+// starts at -136 * sum(a) and gains sum a * (128 + u) = sum a * code
+// + 136 * sum a. The group's fp32 scale multiplies the fp32 group accumulator,
+// so the weights reach the matrix cores exact.
+// The nibble trick emits pairs in the order (0,4) (1,5) (2,6) (3,7) of each
+// 8 codes, so the A rows of routed experts are stored with their 8-element
+// blocks in that order: x by the router kernel (x_perm), H by this kernel's
+// up-projection epilogue. bf16 weights (the shared expert) use natural order.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+constexpr int NT = 256;
+constexpr uint32_t kMagic = 0x43004300u;   // bf16 128.0 in both halves
+constexpr uint32_t kNeg136 = 0xC308C308u;  // bf16 -136.0 in both halves
+}  // namespace
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Weights are read exactly once: non-temporal loads keep them from displacing
+// the reused activations in the vector L1.
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float ld_stream_f(const float* p) { return __builtin_nontemporal_load(p); }
+
+// 8 two's-complement nibbles -> bf16 pairs (128 + u) in the order 0,4 | 1,5 | 2,6 | 3,7
+__device__ __forceinline__ uint4 offset_bf16(uint32_t w) {
+    const uint32_t u = w ^ 0x88888888u;
+    uint4 r;
+    r.x = (u & 0x000F000Fu) | kMagic;
+    r.y = ((u >> 4) & 0x000F000Fu) | kMagic;
+    r.z = ((u >> 8) & 0x000F000Fu) | kMagic;
+    r.w = ((u >> 12) & 0x000F000Fu) | kMagic;
+    return r;
+}
+
+struct RoutedSlot {
+    uint4 w0, w1;
+    float s0, s1;
+    uint4 a[4];
+};
+
+struct SharedSlot {
+    uint4 b0[4], b1[4];
+    uint4 a[4];
+};
+
+// group g of this lane's piece of a 16-row int4 tile (1 KB per tile) and its scale
+template <bool UP>
+__device__ __forceinline__ void load_routed(RoutedSlot& sl, const uint8_t* q0, const uint8_t* q1,
+                                            const float* s0, const float* s1, const uint16_t* arow,
+                                            int g) {
+    sl.w0 = ld_stream(q0 + g * 1024);
+    sl.s0 = ld_stream_f(s0 + g * 16);
+    if (UP) {
+        sl.w1 = ld_stream(q1 + g * 1024);
+        sl.s1 = ld_stream_f(s1 + g * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sl.a[i] = *reinterpret_cast<const uint4*>(arow + g * kGroup + i * 8);
+}
+
+template <bool UP>
+__device__ __forceinline__ void compute_routed(const RoutedSlot& sl, f32x4& acc0, f32x4& acc1) {
+    const bf16x8 neg136 = as_bf16x8(make_uint4(kNeg136, kNeg136, kNeg136, kNeg136));
+    f32x4 corr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sl.a[i]), neg136, corr, 0, 0, 0);
+    const uint32_t w0[4] = {sl.w0.x, sl.w0.y, sl.w0.z, sl.w0.w};
+    f32x4 g0 = corr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        g0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sl.a[i]), as_bf16x8(offset_bf16(w0[i])),
+                                                     g0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc0[r] = fmaf(sl.s0, g0[r], acc0[r]);
+    if (UP) {
+        const uint32_t w1[4] = {sl.w1.x, sl.w1.y, sl.w1.z, sl.w1.w};
+        f32x4 g1 = corr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            g1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sl.a[i]),
+                                                         as_bf16x8(offset_bf16(w1[i])), g1, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc1[r] = fmaf(sl.s1, g1[r], acc1[r]);
+    }
+}
+
+// group g of a step-major bf16 tile (4 steps x 16 rows x 32 columns, 4 KB):
+// step i is 1 KB, this lane's piece is row l16, columns 8*kq .. 8*kq+7
+template <bool UP>
+__device__ __forceinline__ void load_shared(SharedSlot& sl, const uint16_t* h0, const uint16_t* h1,
+                                            const uint16_t* arow, int g) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sl.b0[i] = ld_stream(h0 + g * 2048 + i * 512);
+        if (UP) sl.b1[i] = ld_stream(h1 + g * 2048 + i * 512);
+        sl.a[i] = *reinterpret_cast<const uint4*>(arow + g * kGroup + i * 32);
+    }
+}
+
+template <bool UP>
+__device__ __forceinline__ void compute_shared(const SharedSlot& sl, f32x4& acc0, f32x4& acc1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sl.a[i]), as_bf16x8(sl.b0[i]), acc0,
+                                                       0, 0, 0);
+        if (UP)
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sl.a[i]), as_bf16x8(sl.b1[i]),
+                                                           acc1, 0, 0, 0);
+    }
+}
+
+// DR / DS: groups kept in flight ahead of the one being computed, for int4
+// (routed) and bf16 (shared) weights
+template <bool UP, int DR, int DS>
+__global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
+    const int c = blockIdx.y;
+    if (c >= *a.nchunks) return;
+    const int4 ch = a.chunks[c];
+    const int group = ch.x, row0 = ch.y, nrows = ch.z;
+    const bool routed = group < a.E;
+    const int64_t K = a.K, N = a.N;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int64_t n = static_cast<int64_t>(blockIdx.x) * 64 + wave * 16 + l16;  // B column
+    const int ng = static_cast<int>(K / kGroup);
+
+    // A row of MFMA row l16: routed experts read the interleaved copy, the shared
+    // expert the natural one. Rows past the chunk repeat its last row: their
+    // outputs are never stored, and every lane then loads unconditionally, which
+    // keeps the load counter of the prefetch ring exact. Step i of group g uses
+    // columns 128g + 32kq + 8i.. (int4: this lane's 32 codes) or 128g + 32i + 8kq..
+    // (bf16 step-major tiles).
+    const int m = l16 < nrows ? l16 : nrows - 1;
+    int64_t src;
+    if (UP) src = routed ? a.perm[row0 + m] / a.top_k : row0 + m - a.P;
+    else src = row0 + m;
+    const uint16_t* arow = (routed ? a.a_perm : a.a) + src * K + (routed ? kq * 32 : kq * 8);
+
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    if (routed) {
+        constexpr int D = DR;
+        constexpr int U = D + 1;
+        // tile row block of this lane's feature; tiles of a row block are consecutive
+        const int64_t rb = static_cast<int64_t>(group) * (N / 16) + (n >> 4);
+        const uint8_t* q0 = a.wq0 + rb * ng * 1024 + l16 * 64 + kq * 16;
+        const uint8_t* q1 = UP ? a.wq1 + rb * ng * 1024 + l16 * 64 + kq * 16 : nullptr;
+        const float* s0 = a.ws0 + rb * ng * 16 + l16;
+        const float* s1 = UP ? a.ws1 + rb * ng * 16 + l16 : nullptr;
+        // Ring of U slots, group g in slot g % U. Loads past the last group re-read
+        // it (cache hits), so every loop iteration issues the same loads and the
+        // compiler can wait on exact load counts; full rounds of U groups run
+        // without guards, the last ng % U groups are already in their slots.
+        RoutedSlot sl[U];
+#pragma unroll
+        for (int p = 0; p < D; ++p) load_routed<UP>(sl[p], q0, q1, s0, s1, arow, min(p, ng - 1));
+        const int full = ng - ng % U;
+        for (int g0 = 0; g0 < full; g0 += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                load_routed<UP>(sl[(u + D) % U], q0, q1, s0, s1, arow, min(g0 + u + D, ng - 1));
+                compute_routed<UP>(sl[u], acc0, acc1);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < D; ++u)
+            if (u < ng - full) compute_routed<UP>(sl[u], acc0, acc1);
+    } else {
+        constexpr int D = DS;
+        constexpr int U = D + 1;
+        const int64_t rb = n >> 4;
+        const uint16_t* h0 = a.sh0 + rb * ng * 2048 + l16 * 32 + kq * 8;
+        const uint16_t* h1 = UP ? a.sh1 + rb * ng * 2048 + l16 * 32 + kq * 8 : nullptr;
+        SharedSlot sl[U];
+#pragma unroll
+        for (int p = 0; p < D; ++p) load_shared<UP>(sl[p], h0, h1, arow, min(p, ng - 1));
+        const int full = ng - ng % U;
+        for (int g0 = 0; g0 < full; g0 += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                load_shared<UP>(sl[(u + D) % U], h0, h1, arow, min(g0 + u + D, ng - 1));
+                compute_shared<UP>(sl[u], acc0, acc1);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < D; ++u)
+            if (u < ng - full) compute_shared<UP>(sl[u], acc0, acc1);
+    }
+
+    // D[m][n]: m = 4 * kq + r (token row of the chunk), n = l16 (this lane's feature)
+    // up: routed rows of H are stored with 8-blocks interleaved for the down projection
+    const int64_t hcol = routed ? ((n & ~7LL) | (((n & 3) << 1) | ((n >> 2) & 1))) : n;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int mr = kq * 4 + r;
+        if (mr >= nrows) continue;
+        const int64_t orow = row0 + mr;
+        if (UP) a.h_out[orow * N + hcol] = f32_to_bf16(siluf_(acc0[r]) * acc1[r]);
+        else a.o_out[orow * N + n] = acc0[r];
+    }
+}
+
+hipError_t launch_decode_up(const DecodeArgs& a, int max_chunks, hipStream_t stream) {
+    dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks));
+    hipLaunchKernelGGL((decode_kernel<true, 3, 1>), grid, dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_down(const DecodeArgs& a, int max_chunks, hipStream_t stream) {
+    dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks));
+    hipLaunchKernelGGL((decode_kernel<false, 3, 2>), grid, dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -12,13 +12,36 @@
 //   tile_base[g] first GEMM row-tile of group g for tiles of `tile_rows`
 //                rows: routed experts are groups 0..E-1, the shared expert
 //                (all T tokens) is group E; tile_base[E+1] = total tiles.
+//   chunks       the decode path's row chunks (group, first row, rows) of at
+//                most kDecodeRows rows, and their number in *nchunks.
 // One block per expert. Each block histograms all P ids in LDS, scans, and
-// compacts the pairs of its own expert with wave ballots, so the result does
-// not depend on the order atomics land in. Integer work, a few microseconds.
+// compacts the pairs of its own expert: every thread owns a contiguous segment
+// of pairs, counts its matches, takes its base from a block-wide exclusive
+// scan and writes its matches in order. The result is the stable counting sort
+// whatever order the atomics land in. Integer work, a few microseconds.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
+
+// 32 consecutive ids of [p0, hi) (-1 past hi), loaded 16 bytes at a time so
+// the loads are in flight together
+__device__ __forceinline__ void load32(const int32_t* __restrict__ ids, int64_t p0, int64_t hi,
+                                       int* v) {
+#pragma unroll
+    for (int j = 0; j < 32; j += 4) {
+        if (p0 + j + 4 <= hi) {
+            const int4 q = *reinterpret_cast<const int4*>(ids + p0 + j);
+            v[j] = q.x;
+            v[j + 1] = q.y;
+            v[j + 2] = q.z;
+            v[j + 3] = q.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[j + i] = (p0 + j + i < hi) ? ids[p0 + j + i] : -1;
+        }
+    }
+}
 
 __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict__ ids, int64_t T,
                                                        int top_k, int E, int tile_rows,
@@ -26,7 +49,9 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ tile_base,
                                                        int32_t* __restrict__ perm,
-                                                       int32_t* __restrict__ inv) {
+                                                       int32_t* __restrict__ inv,
+                                                       int4* __restrict__ chunks,
+                                                       int32_t* __restrict__ nchunks) {
     __shared__ int hist[kMaxExperts];
     __shared__ int offs[kMaxExperts + 1];
     __shared__ int wave_tot[4];
@@ -35,10 +60,25 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
     const int wid = tid >> 6;
     const int64_t P = T * top_k;
     const int e = blockIdx.x;
+    // each thread owns a contiguous segment of pairs (a multiple of 4 long)
+    const int64_t seg = ((P + 255) / 256 + 3) & ~static_cast<int64_t>(3);
+    const int64_t lo = min(P, tid * seg);
+    const int64_t hi = min(P, lo + seg);
 
     for (int i = tid; i < E; i += 256) hist[i] = 0;
     __syncthreads();
-    for (int64_t p = tid; p < P; p += 256) atomicAdd(&hist[ids[p]], 1);
+    int mine = 0;  // pairs of expert e in this thread's segment
+    for (int64_t p0 = lo; p0 < hi; p0 += 32) {
+        int v[32];
+        load32(ids, p0, hi, v);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            if (v[j] >= 0) {
+                atomicAdd(&hist[v[j]], 1);
+                mine += v[j] == e;
+            }
+        }
+    }
     __syncthreads();
     if (tid == 0) {
         int run = 0;
@@ -55,6 +95,14 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
             }
             tile_base[E] = tiles;
             tile_base[E + 1] = tiles + static_cast<int>((T + tile_rows - 1) / tile_rows);
+            int n = 0;  // decode chunks: the shared expert first, then routed experts
+            for (int64_t r = 0; r < T; r += kDecodeRows)
+                chunks[n++] = make_int4(E, static_cast<int>(P + r),
+                                        static_cast<int>(min(static_cast<int64_t>(kDecodeRows), T - r)), 0);
+            for (int i = 0; i < E; ++i)
+                for (int r = 0; r < hist[i]; r += kDecodeRows)
+                    chunks[n++] = make_int4(i, offs[i] + r, min(kDecodeRows, hist[i] - r), 0);
+            *nchunks = n;
         }
     }
     __syncthreads();
@@ -65,37 +113,41 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
         }
         if (tid == 0) offsets[E] = offs[E];
     }
-    if (hist[e] == 0) return;
+    if (hist[e] == 0) return;  // block-uniform
 
-    // stable compaction of the pairs routed to expert e
-    int running = offs[e];
-    for (int64_t c0 = 0; c0 < P; c0 += 256) {
-        const int64_t p = c0 + tid;
-        const bool flag = p < P && ids[p] == e;
-        const unsigned long long mask = __ballot(flag);
-        const int rank_in_wave = __popcll(mask & ((1ull << lane) - 1ull));
-        if (lane == 0) wave_tot[wid] = __popcll(mask);
-        __syncthreads();
-        int before = 0;
-        for (int w = 0; w < wid; ++w) before += wave_tot[w];
-        const int total = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
-        if (flag) {
-            const int slot = running + before + rank_in_wave;
-            perm[slot] = static_cast<int32_t>(p);
-            inv[p] = slot;
+    // stable compaction of the pairs routed to expert e: exclusive scan of the
+    // per-thread match counts gives each segment its first slot
+    int incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) wave_tot[wid] = incl;
+    __syncthreads();
+    int slot = offs[e] + incl - mine;
+    for (int w = 0; w < wid; ++w) slot += wave_tot[w];
+    if (mine == 0) return;
+    for (int64_t p0 = lo; p0 < hi; p0 += 32) {
+        int v[32];
+        load32(ids, p0, hi, v);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            if (v[j] == e) {
+                perm[slot] = static_cast<int32_t>(p0 + j);
+                inv[p0 + j] = slot;
+                ++slot;
+            }
         }
-        running += total;
-        __syncthreads();
-        if (running == offs[e] + hist[e]) break;  // block-uniform
     }
 }
 
 hipError_t launch_dispatch(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_rows,
                            int32_t* counts, int32_t* offsets, int32_t* tile_base, int32_t* perm,
-                           int32_t* inv, hipStream_t stream) {
+                           int32_t* inv, int4* chunks, int32_t* nchunks, hipStream_t stream) {
     hipLaunchKernelGGL(dispatch_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, stream, ids,
                        T, top_k, static_cast<int>(E), tile_rows, counts, offsets, tile_base, perm,
-                       inv);
+                       inv, chunks, nchunks);
     return hipGetLastError();
 }
 

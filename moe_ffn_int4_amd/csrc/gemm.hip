@@ -19,13 +19,16 @@
 //         the SwiGLU product is formed in registers
 //   down: O[slot, m]  = (H W2^T)[m]                    (fp32 out)
 //
-// Tiles: 128 rows x 128 columns x 64 reduction per step, 256 threads = 4
-// waves in a 2 x 2 grid, each wave 64 x 64 from 4 x 4 v_mfma_f32_16x16x32_bf16.
-// A and B are staged through LDS (rows padded by 16 bytes so the 16-byte
-// fragment reads are bank-conflict free). Int4 B rows are dequantized on the
-// way into LDS: each thread takes 32 codes of one row (16 bytes, one load),
-// sign-extends the nibbles, multiplies by the group scale in fp32 and rounds
-// to bf16 (round to nearest even). Accumulation is fp32 in the MFMA.
+// Tiles: 128 rows x 128 columns x 128 reduction (one quantization group) per
+// step, 256 threads = 4 waves in a 2 x 2 grid, each wave 64 x 64 from 4 x 4
+// v_mfma_f32_16x16x32_bf16. A and B are staged through LDS (rows padded by 16
+// bytes so the 16-byte fragment reads are bank-conflict free). Weights come in
+// the tiled layouts (moe_quantize_int4_tiled / moe_pack_bf16_tiled): per step
+// the block reads eight whole 16-row tiles, 1 KB (int4) or 4 KB (bf16) each.
+// Int4 B rows are dequantized on the way into LDS: each thread takes 64 codes
+// of one row (32 bytes), sign-extends the nibbles, multiplies by the group
+// scale in fp32 and rounds to bf16 (round to nearest even). Accumulation is
+// fp32 in the MFMA.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,7 +37,7 @@ namespace moe {
 namespace {
 constexpr int BM = kPrefillBM;  // 128 rows (tokens / slots)
 constexpr int BN = 128;         // B rows staged per block (output columns)
-constexpr int BK = 64;          // reduction step
+constexpr int BK = kGroup;      // reduction step: one quantization group
 constexpr int LDK = BK + 8;     // LDS row pitch in bf16 elements
 constexpr int NT = 256;
 }  // namespace
@@ -93,40 +96,46 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GroupedGemmArgs a) {
     const int wm = wid >> 1, wn = wid & 1;
     const int64_t n0 = static_cast<int64_t>(blockIdx.y) * (UP ? BN / 2 : BN);
 
-    // ---- A rows this thread stages: rows (tid + 256 i) / 8, 16-byte column chunk (tid & 7)
-    const uint16_t* arow[4];
+    // ---- A rows this thread stages: rows (tid + 256 i) / 16, 16-byte column piece (tid & 15)
+    constexpr int AP = BM * BK / 8 / NT;  // 16-byte pieces per thread
+    const uint16_t* arow[AP];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid + NT * i) >> 3;
+    for (int i = 0; i < AP; ++i) {
+        const int r = (tid + NT * i) >> 4;
         arow[i] = nullptr;
         if (r < tile.nrows) {
             const int64_t s = tile.row0 + r;
             int64_t src;
             if (UP) src = routed ? a.perm[s] / a.top_k : s - a.P;
             else src = s;
-            arow[i] = a.a + src * K + (tid & 7) * 8;
+            arow[i] = a.a + src * K + (tid & 15) * 8;
         }
     }
 
-    // ---- B rows: int4 path, one row / 32 codes per thread; bf16 path, 4 chunks per thread
+    // ---- B: LDS row r (0..127) is weight row n0 + (r & 63) of W1 / W3 (up) or
+    // n0 + r of W2 (down). Tiles of one 16-row block are consecutive, ng per block.
+    const int64_t ng = K / kGroup;
+    auto row_block = [&](int r) -> int64_t {  // global 16-row block of LDS row r
+        const int64_t n = UP ? n0 + (r & 63) : n0 + r;
+        return n >> 4;
+    };
+    // int4: thread -> LDS row tid/2, 64 codes (32 bytes) at half (tid & 1)
     const int qr = tid >> 1, qh = tid & 1;
     const uint8_t* bq = nullptr;
     const float* bs = nullptr;
-    const uint16_t* bh[4] = {nullptr, nullptr, nullptr, nullptr};
+    // bf16: thread -> piece tid of each of the 8 row blocks' 4 KB tiles
+    const uint16_t* bh[8];
     if (routed) {
-        const int64_t e = tile.group;
-        const int64_t n = UP ? n0 + (qr & 63) : n0 + qr;
+        const int64_t rb = static_cast<int64_t>(tile.group) * (N / 16) + row_block(qr);
         const uint8_t* q = (UP && qr >= 64) ? a.wq1 : a.wq0;
         const float* sc = (UP && qr >= 64) ? a.ws1 : a.ws0;
-        bq = q + (e * N + n) * (K / 2) + qh * 16;
-        bs = sc + (e * N + n) * (K / kGroup);
+        bq = q + rb * ng * 1024 + (qr & 15) * 64 + qh * 32;
+        bs = sc + rb * ng * 16 + (qr & 15);
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (tid + NT * i) >> 3;
-            const int64_t n = UP ? n0 + (r & 63) : n0 + r;
-            const uint16_t* src = (UP && r >= 64) ? a.sh1 : a.sh0;
-            bh[i] = src + n * K + (tid & 7) * 8;
+        for (int i = 0; i < 8; ++i) {
+            const uint16_t* src = (UP && i >= 4) ? a.sh1 : a.sh0;
+            bh[i] = src + row_block(i * 16) * ng * 2048 + tid * 8;
         }
     }
 
@@ -143,43 +152,42 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GroupedGemmArgs a) {
         brow[j] = UP ? ((j < 2) ? wn * 32 + j * 16 : 64 + wn * 32 + (j - 2) * 16) + l16
                      : wn * 64 + j * 16 + l16;
 
-    for (int64_t k0 = 0; k0 < K; k0 += BK) {
-        uint4 av[4];
+    for (int64_t g = 0; g < ng; ++g) {
+        const int64_t k0 = g * BK;
+        uint4 av[AP];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < AP; ++i)
             av[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0) : make_uint4(0, 0, 0, 0);
-        uint4 bv[4];
+        uint4 bv[8];
         float scale = 0.f;
         if (routed) {
-            bv[0] = *reinterpret_cast<const uint4*>(bq + k0 / 2);
-            scale = bs[k0 / kGroup];
+            bv[0] = *reinterpret_cast<const uint4*>(bq + g * 1024);
+            bv[1] = *reinterpret_cast<const uint4*>(bq + g * 1024 + 16);
+            scale = bs[g * 16];
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = *reinterpret_cast<const uint4*>(bh[i] + k0);
+            for (int i = 0; i < 8; ++i) bv[i] = *reinterpret_cast<const uint4*>(bh[i] + g * 2048);
         }
         __syncthreads();  // previous step's fragments are consumed
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (tid + NT * i) >> 3;
-            *reinterpret_cast<uint4*>(&As[r * LDK + (tid & 7) * 8]) = av[i];
+        for (int i = 0; i < AP; ++i) {
+            const int r = (tid + NT * i) >> 4;
+            *reinterpret_cast<uint4*>(&As[r * LDK + (tid & 15) * 8]) = av[i];
         }
         if (routed) {
-            uint32_t d[16];
-            dequant8(bv[0].x, scale, d + 0);
-            dequant8(bv[0].y, scale, d + 4);
-            dequant8(bv[0].z, scale, d + 8);
-            dequant8(bv[0].w, scale, d + 12);
-            uint4* dst = reinterpret_cast<uint4*>(&Bs[qr * LDK + qh * 32]);
-            dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
-            dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
-            dst[2] = make_uint4(d[8], d[9], d[10], d[11]);
-            dst[3] = make_uint4(d[12], d[13], d[14], d[15]);
-        } else {
+            uint32_t d[32];
+            const uint32_t w[8] = {bv[0].x, bv[0].y, bv[0].z, bv[0].w, bv[1].x, bv[1].y, bv[1].z, bv[1].w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = (tid + NT * i) >> 3;
-                *reinterpret_cast<uint4*>(&Bs[r * LDK + (tid & 7) * 8]) = bv[i];
-            }
+            for (int i = 0; i < 8; ++i) dequant8(w[i], scale, d + 4 * i);
+            uint4* dst = reinterpret_cast<uint4*>(&Bs[qr * LDK + qh * 64]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dst[i] = make_uint4(d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]);
+        } else {
+            // piece tid of a step-major tile: step tid/64, row (tid/4)%16, columns 8*(tid%4)
+            const int step = tid >> 6, row = (tid >> 2) & 15, col = step * 32 + (tid & 3) * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<uint4*>(&Bs[(i * 16 + row) * LDK + col]) = bv[i];
         }
         __syncthreads();
 #pragma unroll

@@ -16,21 +16,48 @@ constexpr int kMaxExperts = 256;
 // lays out its tile table for this height.
 constexpr int kPrefillBM = 128;
 
-// K1
+// Rows per decode chunk (the M of one MFMA tile).
+constexpr int kDecodeRows = 16;
+// Largest T * E the one-block small-batch routing keeps in LDS.
+constexpr int kSmallRouteLogits = 8192;
+// Largest T * top_k the one-block small-batch routing handles.
+constexpr int kSmallRoutePairs = 1024;
+
+// K1 (row-major groups, or the 16-row tiles the forward pass reads)
 hipError_t launch_quantize_int4(const float* w, int64_t rows, int64_t K, uint8_t* q,
-                                float* scales, hipStream_t stream);
+                                float* scales, bool tiled, hipStream_t stream);
+// bf16 [rows, K] -> 16 x 128 tiles in MFMA step order (shared expert weights)
+hipError_t launch_pack_bf16(const uint16_t* src, int64_t rows, int64_t K, uint16_t* dst,
+                            hipStream_t stream);
 
-// K2: logits [T, E] = x @ router_w^T (+ b), fp32
-hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* b, int64_t T,
-                                int64_t d, int64_t E, float* logits, hipStream_t stream);
-// K2: top-k per token (ties to the lower id) and sigmoid gates
-hipError_t launch_topk(const float* logits, int64_t T, int64_t E, int top_k, int32_t* ids,
-                       float* gates, int32_t* ids_copy, float* gates_copy, hipStream_t stream);
+// K2: router tiling and reduction split for a batch shape
+struct RouterPlan {
+    int kind;    // tile variant
+    int tt, ee;  // tokens x experts per block
+    int slices;  // reduction slices (split-K); partial sums [slices, T, E]
+};
+RouterPlan router_plan(int64_t T, int64_t d, int64_t E);
+// K2: partials[s][t][e] = sum over slice s of x[t, :] router_w[e, :]   (fp32)
+// (optional) x_perm: x with 8-element blocks in the order 0,4,1,5,2,6,3,7
+hipError_t launch_router_partials(const uint16_t* x, const float* wr, int64_t T, int64_t d,
+                                  int64_t E, const RouterPlan& plan, float* partials,
+                                  uint16_t* x_perm, hipStream_t stream);
+// K2: logits = sum of slices (+ bias), top-k per token (ties to the lower id), sigmoid gates
+hipError_t launch_topk(const float* partials, int slices, const float* bias, int64_t T, int64_t E,
+                       int top_k, float* logits, int32_t* ids, float* gates, int32_t* ids_copy,
+                       float* gates_copy, hipStream_t stream);
+// K2 + K3 for small batches in one block: logits, top-k, gates, counts, offsets,
+// GEMM tile table, perm, inv and the decode row chunks (int4: group, first row, rows, 0)
+hipError_t launch_route_small(const float* partials, int slices, const float* bias, int64_t T,
+                              int64_t E, int top_k, int tile_rows, float* logits, int32_t* ids,
+                              float* gates, int32_t* ids_copy, float* gates_copy, int32_t* counts,
+                              int32_t* offsets, int32_t* tile_base, int32_t* perm, int32_t* inv,
+                              int4* chunks, int32_t* nchunks, hipStream_t stream);
 
-// K3: counts, offsets, GEMM tile table, stable permutation and its inverse
+// K3: counts, offsets, GEMM tile table, stable permutation and its inverse, decode chunks
 hipError_t launch_dispatch(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_rows,
                            int32_t* counts, int32_t* offsets, int32_t* tile_base, int32_t* perm,
-                           int32_t* inv, hipStream_t stream);
+                           int32_t* inv, int4* chunks, int32_t* nchunks, hipStream_t stream);
 
 struct GroupedGemmArgs {
     const uint16_t* a;       // up: x [T, d]; down: H [P + T, h]
@@ -58,6 +85,32 @@ struct GroupedGemmArgs {
 hipError_t launch_grouped_up(const GroupedGemmArgs& args, hipStream_t stream);
 // K5 (routed) + K6b (shared): O = H W2^T, one launch
 hipError_t launch_grouped_down(const GroupedGemmArgs& args, hipStream_t stream);
+
+struct DecodeArgs {
+    const uint16_t* a;       // up: x [T, d]; down: H [P + T, h]
+    const uint16_t* a_perm;  // routed-expert A rows, 8-blocks interleaved (up: x_perm; down: H)
+    int64_t T;
+    int64_t P;
+    int top_k;
+    int E;
+    int64_t K;               // reduction dim
+    int64_t N;               // output features
+    const int32_t* perm;
+    const int4* chunks;      // (group, first row, rows, 0); rows index H / O
+    const int32_t* nchunks;
+    const uint8_t* wq0;
+    const float* ws0;
+    const uint8_t* wq1;
+    const float* ws1;
+    const uint16_t* sh0;
+    const uint16_t* sh1;
+    uint16_t* h_out;
+    float* o_out;
+};
+
+// K7: decode up / down projections over the row chunks
+hipError_t launch_decode_up(const DecodeArgs& a, int max_chunks, hipStream_t stream);
+hipError_t launch_decode_down(const DecodeArgs& a, int max_chunks, hipStream_t stream);
 
 // K6c: y[t] = O[P + t] + sum_j gate[t, j] * O[inv[t, j]]  -> bf16
 hipError_t launch_combine(const float* O, const float* gates, const int32_t* inv, int64_t T,

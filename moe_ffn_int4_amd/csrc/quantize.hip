@@ -13,13 +13,18 @@
 // library is compiled with -fhip-fp32-correctly-rounded-divide-sqrt and no
 // fast-math), rintf maps to round-half-even, so codes and scales are
 // bit-identical to the fp32 definition.
+//
+// TILED = true writes the storage order the forward pass reads: tile
+// t = (row/16) * (K/128) + group holds the group's 64 bytes for 16 rows
+// (1 KB) and its 16 scales, so one wavefront access covers one tile.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
+template <bool TILED>
 __global__ __launch_bounds__(256) void quantize_int4_kernel(const float4* __restrict__ w,
-                                                            int64_t ngroups,
+                                                            int64_t ngroups, int64_t groups_per_row,
                                                             uint16_t* __restrict__ q16,
                                                             float* __restrict__ scales) {
     const int lane = threadIdx.x & 63;
@@ -48,21 +53,59 @@ __global__ __launch_bounds__(256) void quantize_int4_kernel(const float4* __rest
             packed |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xFu) << (4 * i);
         }
         if (valid) {
-            q16[g * 32 + hl] = static_cast<uint16_t>(packed);
-            if (hl == 0) scales[g] = s;
+            int64_t at = g;  // row-major: group g of the flattened [rows, K/128]
+            if (TILED) {
+                const int64_t r = g / groups_per_row, gg = g - r * groups_per_row;
+                at = ((r >> 4) * groups_per_row + gg) * 16 + (r & 15);
+            }
+            q16[at * 32 + hl] = static_cast<uint16_t>(packed);
+            if (hl == 0) scales[at] = s;
         }
     }
 }
 
 hipError_t launch_quantize_int4(const float* w, int64_t rows, int64_t K, uint8_t* q,
-                                float* scales, hipStream_t stream) {
+                                float* scales, bool tiled, hipStream_t stream) {
     const int64_t ngroups = rows * (K / kGroup);
     if (ngroups == 0) return hipSuccess;
     const int64_t want = (ngroups + 7) / 8;  // 8 groups per 256-thread block per pass
     const int blocks = static_cast<int>(want < 8192 ? want : 8192);
-    hipLaunchKernelGGL(quantize_int4_kernel, dim3(blocks), dim3(256), 0, stream,
-                       reinterpret_cast<const float4*>(w), ngroups,
-                       reinterpret_cast<uint16_t*>(q), scales);
+    if (tiled)
+        hipLaunchKernelGGL(quantize_int4_kernel<true>, dim3(blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const float4*>(w), ngroups, K / kGroup,
+                           reinterpret_cast<uint16_t*>(q), scales);
+    else
+        hipLaunchKernelGGL(quantize_int4_kernel<false>, dim3(blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const float4*>(w), ngroups, K / kGroup,
+                           reinterpret_cast<uint16_t*>(q), scales);
+    return hipGetLastError();
+}
+
+// bf16 [rows, K] -> tiles of 16 rows x 128 columns stored as 4 steps of 32
+// columns (the B-operand order of one 16x16x32 MFMA step per 1 KB). One
+// thread per destination 16-byte piece; reads and writes are both 16 bytes.
+__global__ __launch_bounds__(256) void pack_bf16_kernel(const uint4* __restrict__ src, int64_t K,
+                                                        int64_t n16, uint4* __restrict__ dst) {
+    const int64_t ng = K / kGroup;
+    for (int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < n16;
+         j += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t t = j >> 8;           // 256 pieces per tile
+        const int within = static_cast<int>(j & 255);
+        const int step = within >> 6, row = (within >> 2) & 15, piece = within & 3;
+        const int64_t rb = t / ng, g = t - rb * ng;
+        const int64_t k = g * kGroup + step * 32 + piece * 8;
+        dst[j] = src[((rb * 16 + row) * K + k) / 8];
+    }
+}
+
+hipError_t launch_pack_bf16(const uint16_t* src, int64_t rows, int64_t K, uint16_t* dst,
+                            hipStream_t stream) {
+    const int64_t n16 = rows * K / 8;
+    if (n16 == 0) return hipSuccess;
+    const int64_t want = (n16 + 255) / 256;
+    const int blocks = static_cast<int>(want < 16384 ? want : 16384);
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4*>(src), K, n16, reinterpret_cast<uint4*>(dst));
     return hipGetLastError();
 }
 

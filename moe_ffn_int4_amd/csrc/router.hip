@@ -8,37 +8,61 @@
 // Logits stay fp32 (the bf16 x widens exactly, router weights are fp32, fp32
 // FMA accumulation): the choice of experts must not move with a cheaper
 // precision, so this small GEMM runs on the vector ALUs, not on bf16 MFMA.
-// Tiling: 32 tokens x 64 experts per 256-thread block, reduction staged through
-// LDS in chunks of 32; each thread owns 2 tokens x 4 experts. Router weights
-// (E x d fp32, 2.6 MB at E = 128) stay in L2 across token tiles.
+//
+// router_partials_kernel<TT, EE, MT, ME>: a 256-thread block computes a
+// TT-token x EE-expert tile over one slice of the reduction dimension; each
+// thread owns MT tokens x ME experts (experts strided so LDS reads are
+// conflict-free). Slices (split-K) give small batches enough blocks; partial
+// sums go to partials[s][t][e] and are added in slice order by the consumer,
+// so the result does not depend on scheduling.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
 namespace {
-constexpr int RT = 32;   // tokens per block
-constexpr int RE = 64;   // experts per block
-constexpr int RK = 32;   // reduction chunk
+constexpr int RK = 32;  // reduction chunk staged in LDS
 }  // namespace
 
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const float* __restrict__ wr,
-                                                            const float* __restrict__ bias,
-                                                            int64_t T, int64_t d, int64_t E,
-                                                            float* __restrict__ logits) {
-    __shared__ float xs[RT][RK + 1];
-    __shared__ float ws[RE][RK + 1];
+template <int TT, int EE, int MT, int ME>
+__global__ __launch_bounds__(256) void router_partials_kernel(const uint16_t* __restrict__ x,
+                                                              const float* __restrict__ wr,
+                                                              int64_t T, int64_t d, int64_t E,
+                                                              int64_t slice,
+                                                              float* __restrict__ partials,
+                                                              uint16_t* __restrict__ x_perm) {
+    static_assert((TT / MT) * (EE / ME) == 256, "one output micro-tile per thread");
+    __shared__ float xs[TT][RK + 1];
+    __shared__ float ws[EE][RK + 1];
     const int tid = threadIdx.x;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT;
-    const int64_t e0 = static_cast<int64_t>(blockIdx.y) * RE;
-    const int tl = tid >> 4;  // tokens 2*tl, 2*tl+1
-    const int el = tid & 15;  // experts el + 16*j
-    float acc[2][4] = {};
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TT;
+    const int64_t e0 = static_cast<int64_t>(blockIdx.y) * EE;
+    const int64_t kb = static_cast<int64_t>(blockIdx.z) * slice;
+    constexpr int EW = EE / ME;  // threads along experts
+    const int tt = tid / EW;     // tokens tt*MT + i
+    const int ee = tid % EW;     // experts ee + EW*j
+    float acc[MT][ME] = {};
 
-    for (int64_t k0 = 0; k0 < d; k0 += RK) {
-        {   // x chunk: 32 x 32 bf16, 4 per thread
-            const int r = tid >> 3, c = (tid & 7) * 4;
+    // x with 8-element blocks stored in the order 0,4,1,5,2,6,3,7: the A operand
+    // layout of the decode path's int4 nibble-pair dequantization
+    if (x_perm && blockIdx.y == 0) {
+        for (int64_t idx = tid; idx < static_cast<int64_t>(TT) * (slice / 8); idx += 256) {
+            const int64_t t = t0 + idx / (slice / 8);
+            if (t >= T) break;
+            const int64_t col = kb + (idx % (slice / 8)) * 8;
+            const uint4 v = *reinterpret_cast<const uint4*>(x + t * d + col);
+            uint4 r;
+            r.x = (v.x & 0xFFFFu) | (v.z << 16);
+            r.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+            r.z = (v.y & 0xFFFFu) | (v.w << 16);
+            r.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+            *reinterpret_cast<uint4*>(x_perm + t * d + col) = r;
+        }
+    }
+
+    for (int64_t k0 = kb; k0 < kb + slice; k0 += RK) {
+        for (int idx = tid; idx < TT * (RK / 4); idx += 256) {  // x: TT x 32 bf16
+            const int r = idx / (RK / 4), c = (idx % (RK / 4)) * 4;
             const int64_t t = t0 + r;
             uint2 v = make_uint2(0u, 0u);
             if (t < T) v = *reinterpret_cast<const uint2*>(x + t * d + k0 + c);
@@ -47,10 +71,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
             xs[r][c + 2] = __uint_as_float(v.y << 16);
             xs[r][c + 3] = __uint_as_float(v.y & 0xFFFF0000u);
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {  // router chunk: 64 x 32 fp32, 8 per thread
-            const int idx = tid + 256 * i;
-            const int r = idx >> 3, c = (idx & 7) * 4;
+        for (int idx = tid; idx < EE * (RK / 4); idx += 256) {  // router: EE x 32 fp32
+            const int r = idx / (RK / 4), c = (idx % (RK / 4)) * 4;
             const int64_t e = e0 + r;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (e < E) v = *reinterpret_cast<const float4*>(wr + e * d + k0 + c);
@@ -62,44 +84,99 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
         __syncthreads();
 #pragma unroll 8
         for (int kk = 0; kk < RK; ++kk) {
-            const float xa = xs[2 * tl][kk], xb = xs[2 * tl + 1][kk];
+            float xv[MT], wv[ME];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float w = ws[el + 16 * j][kk];
-                acc[0][j] = fmaf(xa, w, acc[0][j]);
-                acc[1][j] = fmaf(xb, w, acc[1][j]);
-            }
+            for (int i = 0; i < MT; ++i) xv[i] = xs[tt * MT + i][kk];
+#pragma unroll
+            for (int j = 0; j < ME; ++j) wv[j] = ws[ee + EW * j][kk];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < ME; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
         }
         __syncthreads();
     }
+    float* out = partials + static_cast<int64_t>(blockIdx.z) * T * E;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t t = t0 + 2 * tl + i;
+    for (int i = 0; i < MT; ++i) {
+        const int64_t t = t0 + tt * MT + i;
         if (t >= T) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t e = e0 + el + 16 * j;
-            if (e < E) logits[t * E + e] = acc[i][j] + (bias ? bias[e] : 0.0f);
+        for (int j = 0; j < ME; ++j) {
+            const int64_t e = e0 + ee + EW * j;
+            if (e < E) out[t * E + e] = acc[i][j];
         }
     }
 }
 
-// One wave per token: k rounds of a wave-wide arg-max over (logit, -id).
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T,
-                                                   int64_t E, int top_k, int32_t* __restrict__ ids,
-                                                   float* __restrict__ gates,
-                                                   int32_t* __restrict__ ids_copy,
-                                                   float* __restrict__ gates_copy) {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-    if (t >= T) return;
+RouterPlan router_plan(int64_t T, int64_t d, int64_t E) {
+    RouterPlan p{};
+    if (T <= 16 && E <= 16) {
+        p.kind = 0;
+        p.tt = 16;
+        p.ee = 16;
+    } else if (E <= 16) {
+        p.kind = 1;
+        p.tt = 128;
+        p.ee = 16;
+    } else if (E <= 32) {
+        p.kind = 2;
+        p.tt = 64;
+        p.ee = 32;
+    } else {
+        p.kind = 3;
+        p.tt = 32;
+        p.ee = 64;
+    }
+    const int64_t tiles = ((T + p.tt - 1) / p.tt) * ((E + p.ee - 1) / p.ee);
+    // enough blocks to cover the chip; slices are whole multiples of 128 wide
+    const int64_t want = (512 + tiles - 1) / tiles;
+    int64_t s = 1;
+    for (int64_t c = 1; c <= d / 128; ++c)
+        if ((d / 128) % c == 0 && c <= want) s = c;
+    p.slices = static_cast<int>(s);
+    return p;
+}
+
+hipError_t launch_router_partials(const uint16_t* x, const float* wr, int64_t T, int64_t d,
+                                  int64_t E, const RouterPlan& p, float* partials,
+                                  uint16_t* x_perm, hipStream_t stream) {
+    dim3 grid(static_cast<unsigned>((T + p.tt - 1) / p.tt), static_cast<unsigned>((E + p.ee - 1) / p.ee),
+              static_cast<unsigned>(p.slices));
+    const int64_t slice = d / p.slices;
+    switch (p.kind) {
+        case 0:
+            hipLaunchKernelGGL((router_partials_kernel<16, 16, 1, 1>), grid, dim3(256), 0, stream, x,
+                               wr, T, d, E, slice, partials, x_perm);
+            break;
+        case 1:
+            hipLaunchKernelGGL((router_partials_kernel<128, 16, 8, 1>), grid, dim3(256), 0, stream, x,
+                               wr, T, d, E, slice, partials, x_perm);
+            break;
+        case 2:
+            hipLaunchKernelGGL((router_partials_kernel<64, 32, 4, 2>), grid, dim3(256), 0, stream, x,
+                               wr, T, d, E, slice, partials, x_perm);
+            break;
+        default:
+            hipLaunchKernelGGL((router_partials_kernel<32, 64, 2, 4>), grid, dim3(256), 0, stream, x,
+                               wr, T, d, E, slice, partials, x_perm);
+            break;
+    }
+    return hipGetLastError();
+}
+
+// One wave per token: sums the slices' partial logits (slice order) plus the
+// bias, then k rounds of a wave-wide arg-max over (logit, lower id first).
+__device__ __forceinline__ void topk_wave(const float* v_in, int64_t E, int top_k, int lane,
+                                          int32_t* ids_out, float* gates_out,
+                                          int32_t* ids_copy, float* gates_copy) {
     constexpr int PER = kMaxExperts / 64;
     float v[PER];
     bool taken[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int64_t e = lane + 64 * i;
-        v[i] = e < E ? logits[t * E + e] : 0.0f;
+        v[i] = e < E ? v_in[e] : 0.0f;
         taken[i] = e >= E;
     }
     for (int j = 0; j < top_k; ++j) {
@@ -107,10 +184,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         int bid = 0x7FFFFFFF;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int e = lane + 64 * i;
             if (!taken[i] && (bid == 0x7FFFFFFF || v[i] > best)) {
                 best = v[i];
-                bid = e;
+                bid = lane + 64 * i;
             }
         }
 #pragma unroll
@@ -129,26 +205,148 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
             if (lane + 64 * i == bid) taken[i] = true;
         if (lane == 0) {
             const float g = 1.0f / (1.0f + expf(-best));
-            ids[t * top_k + j] = bid;
-            gates[t * top_k + j] = g;
-            if (ids_copy) ids_copy[t * top_k + j] = bid;
-            if (gates_copy) gates_copy[t * top_k + j] = g;
+            ids_out[j] = bid;
+            gates_out[j] = g;
+            if (ids_copy) ids_copy[j] = bid;
+            if (gates_copy) gates_copy[j] = g;
         }
     }
 }
 
-hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* b, int64_t T,
-                                int64_t d, int64_t E, float* logits, hipStream_t stream) {
-    dim3 grid(static_cast<unsigned>((T + RT - 1) / RT), static_cast<unsigned>((E + RE - 1) / RE));
-    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, x, wr, b, T, d, E, logits);
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partials, int slices,
+                                                   const float* __restrict__ bias, int64_t T,
+                                                   int64_t E, int top_k, float* __restrict__ logits,
+                                                   int32_t* __restrict__ ids,
+                                                   float* __restrict__ gates,
+                                                   int32_t* __restrict__ ids_copy,
+                                                   float* __restrict__ gates_copy) {
+    __shared__ float row[4][kMaxExperts];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
+    if (t >= T) return;  // wave-uniform; no block-wide barrier below
+    for (int64_t e = lane; e < E; e += 64) {
+        float s = 0.0f;
+        int i = 0;
+        for (; i + 4 <= slices; i += 4) {  // independent loads, summed in slice order
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = partials[(static_cast<int64_t>(i + j) * T + t) * E + e];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s += v[j];
+        }
+        for (; i < slices; ++i) s += partials[(static_cast<int64_t>(i) * T + t) * E + e];
+        if (bias) s += bias[e];
+        row[w][e] = s;
+        logits[t * E + e] = s;
+    }
+    __builtin_amdgcn_wave_barrier();
+    topk_wave(row[w], E, top_k, lane, ids + t * top_k, gates + t * top_k,
+              ids_copy ? ids_copy + t * top_k : nullptr, gates_copy ? gates_copy + t * top_k : nullptr);
+}
+
+hipError_t launch_topk(const float* partials, int slices, const float* bias, int64_t T, int64_t E,
+                       int top_k, float* logits, int32_t* ids, float* gates, int32_t* ids_copy,
+                       float* gates_copy, hipStream_t stream) {
+    const unsigned blocks = static_cast<unsigned>((T + 3) / 4);  // 4 waves (tokens) per block
+    hipLaunchKernelGGL(topk_kernel, dim3(blocks), dim3(256), 0, stream, partials, slices, bias, T, E,
+                       top_k, logits, ids, gates, ids_copy, gates_copy);
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, int64_t T, int64_t E, int top_k, int32_t* ids,
-                       float* gates, int32_t* ids_copy, float* gates_copy, hipStream_t stream) {
-    const unsigned blocks = static_cast<unsigned>((T + 3) / 4);  // 4 waves (tokens) per block
-    hipLaunchKernelGGL(topk_kernel, dim3(blocks), dim3(256), 0, stream, logits, T, E, top_k, ids,
-                       gates, ids_copy, gates_copy);
+// ------------------------------------------------------------------------
+// Small-batch routing in one block: logits (slice sums + bias), top-k and
+// gates, then the dispatch (counts, offsets, stable perm / inv) and the list
+// of decode row chunks (<= 16 rows each; routed experts in id order, then the
+// shared expert). Used when T * E <= kSmallRouteLogits and T * top_k <= 1024.
+__global__ __launch_bounds__(256) void route_small_kernel(
+    const float* __restrict__ partials, int slices, const float* __restrict__ bias, int64_t T,
+    int E, int top_k, int tile_rows, float* __restrict__ logits, int32_t* __restrict__ ids,
+    float* __restrict__ gates, int32_t* __restrict__ ids_copy, float* __restrict__ gates_copy,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_base,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int4* __restrict__ chunks,
+    int32_t* __restrict__ nchunks) {
+    __shared__ float lg[kSmallRouteLogits];
+    __shared__ int sids[1024];
+    __shared__ float sg[1024];
+    __shared__ int cnt[kMaxExperts], off[kMaxExperts + 1];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t TE = T * E;
+    const int P = static_cast<int>(T) * top_k;
+    for (int64_t i = tid; i < TE; i += 256) {
+        float s = 0.0f;
+        int k = 0;
+        for (; k + 8 <= slices; k += 8) {  // 8 independent loads in flight, summed in order
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = partials[(k + j) * TE + i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s += v[j];
+        }
+        for (; k < slices; ++k) s += partials[k * TE + i];
+        if (bias) s += bias[i % E];
+        lg[i] = s;
+        logits[i] = s;
+    }
+    __syncthreads();
+    for (int64_t t = w; t < T; t += 4)
+        topk_wave(lg + t * E, E, top_k, lane, sids + t * top_k, sg + t * top_k,
+                  ids_copy ? ids_copy + t * top_k : nullptr,
+                  gates_copy ? gates_copy + t * top_k : nullptr);
+    __syncthreads();
+    for (int p = tid; p < P; p += 256) {
+        ids[p] = sids[p];
+        gates[p] = sg[p];
+    }
+    if (tid == 0) {
+        for (int e = 0; e < E; ++e) cnt[e] = 0;
+        for (int p = 0; p < P; ++p) cnt[sids[p]]++;
+        int run = 0;
+        for (int e = 0; e < E; ++e) {
+            off[e] = run;
+            run += cnt[e];
+        }
+        off[E] = run;
+        for (int e = 0; e < E; ++e) cnt[e] = 0;  // reuse as running rank
+        for (int p = 0; p < P; ++p) {
+            const int e = sids[p];
+            const int slot = off[e] + cnt[e]++;
+            perm[slot] = p;
+            inv[p] = slot;
+        }
+        int n = 0;  // shared expert first (the largest work items), then routed experts
+        for (int r = 0; r < T; r += kDecodeRows)
+            chunks[n++] = make_int4(E, P + r, static_cast<int>(T) - r < kDecodeRows ? static_cast<int>(T) - r
+                                                                             : kDecodeRows, 0);
+        for (int e = 0; e < E; ++e) {
+            const int c = off[e + 1] - off[e];
+            for (int r = 0; r < c; r += kDecodeRows)
+                chunks[n++] = make_int4(e, off[e] + r, c - r < kDecodeRows ? c - r : kDecodeRows, 0);
+        }
+        *nchunks = n;
+        int tiles = 0;
+        for (int e = 0; e < E; ++e) {
+            tile_base[e] = tiles;
+            tiles += (off[e + 1] - off[e] + tile_rows - 1) / tile_rows;
+        }
+        tile_base[E] = tiles;
+        tile_base[E + 1] = tiles + static_cast<int>((T + tile_rows - 1) / tile_rows);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) {
+        counts[e] = off[e + 1] - off[e];
+        offsets[e] = off[e];
+    }
+    if (tid == 0) offsets[E] = off[E];
+}
+
+hipError_t launch_route_small(const float* partials, int slices, const float* bias, int64_t T,
+                              int64_t E, int top_k, int tile_rows, float* logits, int32_t* ids,
+                              float* gates, int32_t* ids_copy, float* gates_copy, int32_t* counts,
+                              int32_t* offsets, int32_t* tile_base, int32_t* perm, int32_t* inv,
+                              int4* chunks, int32_t* nchunks, hipStream_t stream) {
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(256), 0, stream, partials, slices, bias, T,
+                       static_cast<int>(E), top_k, tile_rows, logits, ids, gates, ids_copy,
+                       gates_copy, counts, offsets, tile_base, perm, inv, chunks, nchunks);
     return hipGetLastError();
 }
 

@@ -58,8 +58,10 @@ def build_layer(cfg: W.MoEConfig, dev="cuda:0", routed_draw: Optional[str] = Non
         ex.quantize_expert(e, *ws)
         del ws
     torch.cuda.synchronize(dev)
+    shared_d = moe.pack_shared(*(s.to(dev) for s in shared))
+    torch.cuda.synchronize(dev)
     return Layer(cfg, x, wr, b, shared, routed_draw, dev, x.to(dev), wr.to(dev),
-                 None if b is None else b.to(dev), tuple(s.to(dev) for s in shared), ex)
+                 None if b is None else b.to(dev), shared_d, ex)
 
 
 def oracle_expert(layer: Layer, e: int) -> Int4Expert:

@@ -36,7 +36,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for need in ("moe_quantize_int4", "moe_forward", "moe_forward_path", "moe_route",
+    for need in ("moe_quantize_int4", "moe_quantize_int4_tiled", "moe_pack_bf16_tiled",
+                 "moe_forward", "moe_forward_path", "moe_route",
                  "moe_forward_workspace_bytes", "moe_route_workspace_bytes",
                  "moe_status_string", "moe_last_error", "moe_abi_version", "moe_device_check"):
         assert need in names
@@ -141,6 +142,20 @@ def test_quantize_validation(L):
     assert L.moe_quantize_int4(FAKE, 4, 256, 128, None, FAKE, None) == INVALID
     assert L.moe_quantize_int4(FAKE, 4, 256, 128, FAKE, FAKE + 1, None) == INVALID
     assert L.moe_quantize_int4(FAKE, 0, 256, 128, FAKE, FAKE, None) == OK  # nothing to do
+
+
+def test_tiled_quantize_and_pack_validation(L):
+    assert L.moe_quantize_int4_tiled(FAKE, 20, 256, 128, FAKE, FAKE, None) == INVALID
+    assert "multiple of 16" in L.moe_last_error().decode()
+    assert L.moe_quantize_int4_tiled(FAKE, 32, 200, 128, FAKE, FAKE, None) == INVALID
+    assert L.moe_quantize_int4_tiled(FAKE, 32, 256, 128, FAKE + 4, FAKE, None) == INVALID
+    assert L.moe_quantize_int4_tiled(FAKE, 0, 256, 128, FAKE, FAKE, None) == OK
+    assert L.moe_pack_bf16_tiled(FAKE, 16, 100, FAKE * 64, None) == INVALID
+    assert L.moe_pack_bf16_tiled(FAKE, 17, 128, FAKE * 64, None) == INVALID
+    assert L.moe_pack_bf16_tiled(FAKE, 16, 128, FAKE + 64, None) == INVALID  # overlap
+    assert "overlap" in L.moe_last_error().decode()
+    assert L.moe_pack_bf16_tiled(None, 16, 128, FAKE, None) == INVALID
+    assert L.moe_pack_bf16_tiled(FAKE, 0, 128, FAKE, None) == OK
 
 
 def test_route_validation(L):

@@ -75,3 +75,45 @@ def test_full_size_expert_matrix():
     c_ref, s_ref = native.quantize_int4(w.cpu().numpy())
     np.testing.assert_array_equal(moe.unpack_int4(q.cpu()).numpy(), c_ref)
     np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,K", [(16, 128), (48, 384), (160, 5120)])
+def test_tiled_layout_holds_the_same_codes(rows, K):
+    """moe_quantize_int4_tiled: same codes and scales, 16-row tile order."""
+    say(f"quantize tiled: rows={rows} K={K}")
+    rng = np.random.default_rng(rows + K)
+    w = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
+    w[3::7] *= np.float32(1e-5)
+    q, s = moe.quantize_int4(torch.from_numpy(w).to(DEV), tiled=True)
+    torch.cuda.synchronize()
+    codes = moe.unpack_int4(moe.untile_int4(q.cpu(), rows, K)).numpy()
+    scales = moe.untile_scales(s.cpu(), rows, K).numpy()
+    _assert_same(w, codes, scales)
+    # spot-check the documented address formula on raw bytes
+    qb, sb = q.cpu().numpy().reshape(-1), s.cpu().numpy().reshape(-1)
+    c_ref, s_ref = int4_group_quantize(w)
+    for (r, k) in [(0, 0), (rows - 1, K - 1), (17 % rows, 130 % K), (rows // 2, K // 2 + 3)]:
+        t = (r // 16) * (K // 128) + k // 128
+        byte = int(qb[t * 1024 + (r % 16) * 64 + (k % 128) // 2])
+        nib = (byte >> 4) if k % 2 else (byte & 15)
+        assert (nib - 16 if nib >= 8 else nib) == c_ref[r, k]
+        assert sb[t * 16 + r % 16] == s_ref[r, k // 128]
+
+
+def test_tiled_rejects_ragged_rows():
+    with pytest.raises(moe.MoEError):
+        moe.quantize_int4(torch.zeros(20, 128, device=DEV), tiled=True)
+
+
+@pytest.mark.parametrize("rows,K", [(16, 128), (48, 384), (8192, 5120)])
+def test_pack_bf16_tiled(rows, K):
+    say(f"pack bf16: rows={rows} K={K}")
+    src = torch.randn(rows, K, device=DEV).to(torch.bfloat16)
+    dst = moe.pack_bf16_tiled(src)
+    torch.cuda.synchronize()
+    assert torch.equal(moe.untile_bf16(dst, rows, K), src)
+    flat, ref = dst.reshape(-1).cpu(), src.cpu()
+    for (r, k) in [(0, 0), (rows - 1, K - 1), (5, 37 % K), (rows // 2, K // 2 + 9)]:
+        t = (r // 16) * (K // 128) + k // 128
+        at = t * 2048 + ((k % 128) // 32) * 512 + (r % 16) * 32 + (k % 32)
+        assert flat[at] == ref[r, k]

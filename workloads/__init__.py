@@ -22,9 +22,10 @@ Distributions (all seeded, seed 0 unless a caller overrides it):
 Random streams: every tensor (and every expert of a routed tensor) has its own
 ``torch.Generator`` seeded from ``(seed, tensor id, expert)`` through a
 splitmix64 mix. Values depend on the generator's device: torch's CPU and GPU
-generators are different algorithms. Small tensors are always drawn on the CPU;
-routed expert weights are drawn on whichever device the caller names, and a
-parity check that needs them on the host copies the device draw back.
+generators are different algorithms. x and the router are always drawn on the
+CPU; expert weights (routed and shared) are drawn on whichever device the caller
+names, and a parity check that needs them on the host copies the device draw
+back.
 """
 from __future__ import annotations
 
@@ -151,12 +152,13 @@ def gen_expert_weight(cfg: MoEConfig, which: str, expert: int, device="cpu") -> 
                        device=device) * 0.02
 
 
-def gen_shared(cfg: MoEConfig):
-    """Shared expert weights S1 [h, d], S3 [h, d], S2 [d, h] in bf16 (CPU)."""
+def gen_shared(cfg: MoEConfig, device="cpu"):
+    """Shared expert weights S1 [h, d], S3 [h, d], S2 [d, h] in bf16 on ``device``
+    (drawn by that device's generator, like the routed weights)."""
     out = []
     for tid, shape in ((S1, (cfg.h, cfg.d)), (S3, (cfg.h, cfg.d)), (S2, (cfg.d, cfg.h))):
-        g = _gen(cfg.seed, tid, 0, "cpu")
-        out.append((torch.randn(*shape, generator=g, dtype=torch.float32) * 0.02)
+        g = _gen(cfg.seed, tid, 0, device)
+        out.append((torch.randn(*shape, generator=g, dtype=torch.float32, device=device) * 0.02)
                    .to(torch.bfloat16))
     return tuple(out)
 
