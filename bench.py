@@ -53,7 +53,33 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--stage-timing", default="separate", choices=["separate", "inline"],
+                    help="per-kernel HIP events in a second pass (separate) or in the timed "
+                         "loop itself (inline)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each layer copy's forward as a captured HIP graph")
     return ap.parse_args()
+
+
+STAGE_TRAFFIC_KEY = {"decode_up": "decode_up"}
+
+
+def measured_traffic(stage: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic.json), or None if there is none for this kernel and
+    workload or the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    key = STAGE_TRAFFIC_KEY.get(stage)
+    if key is None or not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(key)
+    if not rec or rec.get("workload") != workload:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
 
 
 def layer_weight_bytes(cfg) -> int:
@@ -187,16 +213,50 @@ def main() -> int:
     print(f"[bench] warmup done; experts touched per layer copy: "
           f"{[int((c > 0).sum()) for c in counts]}", file=sys.stderr, flush=True)
 
-    moe.profile_enable(True)
+    graphs = None
+    if args.graph:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(nlayers):  # capture one forward per layer copy
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(i)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        for i in range(warmup):
+            graphs[i % nlayers].replay()
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs is not None:
+            graphs[i % nlayers].replay()
+        else:
+            step(i)
+
+    inline = args.stage_timing == "inline"
+    moe.profile_enable(inline)
     moe.profile_read()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    stages = moe.profile_read()
-    moe.profile_enable(False)
+    if inline:
+        stages = moe.profile_read()
+        moe.profile_enable(False)
+    else:
+        # the same steps again, eagerly, with a HIP event recorded around every
+        # kernel launch on the forward's stream: per-kernel durations
+        moe.profile_enable(True)
+        moe.profile_read()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        stages = moe.profile_read()
+        moe.profile_enable(False)
     wall = t1 - t0
     ms_per_step = wall * 1e3 / steps
     value = cfg0.T * steps / wall
@@ -220,6 +280,9 @@ def main() -> int:
         achieved = flops / mean_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None}
+    roof["traffic"] = measured_traffic(dom, cfg0.name)
+    if roof["traffic"] is not None:
+        roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
     roof["kernel"] = dom
     roof["mean_launch_us"] = mean_s * 1e6
     roof["algorithmic_per_launch"] = byts if decode_like else flops
@@ -232,6 +295,8 @@ def main() -> int:
         "touched_experts": [u["touched"] for u in units],
         "layer_copies": nlayers,
         "path": args.path,
+        "graph": bool(args.graph),
+        "stage_timing": args.stage_timing,
     }
 
     if args.copy_calibration:

@@ -69,6 +69,11 @@ struct RoutedSlot {
     uint4 a[4];
 };
 
+struct WeightSlot {
+    uint4 w0, w1;
+    float s0, s1;
+};
+
 struct SharedSlot {
     uint4 b0[4], b1[4];
     uint4 a[4];
@@ -119,6 +124,31 @@ __device__ __forceinline__ void compute_routed(const RoutedSlot& sl, f32x4& acc0
 // group g of a step-major bf16 tile (4 steps x 16 rows x 32 columns, 4 KB):
 // step i is 1 KB, this lane's piece is row l16, columns 8*kq .. 8*kq+7
 template <bool UP>
+__device__ __forceinline__ void load_weights(WeightSlot& sl, const uint8_t* q0, const uint8_t* q1,
+                                             const float* s0, const float* s1, int g) {
+    sl.w0 = ld_stream(q0 + g * 1024);
+    sl.s0 = ld_stream_f(s0 + g * 16);
+    if (UP) {
+        sl.w1 = ld_stream(q1 + g * 1024);
+        sl.s1 = ld_stream_f(s1 + g * 16);
+    }
+}
+
+// one int4 group with A fragments from LDS (row `lrow` of the staged chunk)
+template <bool UP>
+__device__ __forceinline__ void compute_lds(const WeightSlot& w, const uint16_t* lrow, int g,
+                                            f32x4& acc0, f32x4& acc1) {
+    RoutedSlot sl;
+    sl.w0 = w.w0;
+    sl.w1 = w.w1;
+    sl.s0 = w.s0;
+    sl.s1 = w.s1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sl.a[i] = *reinterpret_cast<const uint4*>(lrow + g * kGroup + i * 8);
+    compute_routed<UP>(sl, acc0, acc1);
+}
+
+template <bool UP>
 __device__ __forceinline__ void load_shared(SharedSlot& sl, const uint16_t* h0, const uint16_t* h1,
                                             const uint16_t* arow, int g) {
 #pragma unroll
@@ -143,8 +173,10 @@ __device__ __forceinline__ void compute_shared(const SharedSlot& sl, f32x4& acc0
 
 // DR / DS: groups kept in flight ahead of the one being computed, for int4
 // (routed) and bf16 (shared) weights
-template <bool UP, int DR, int DS>
+template <bool UP, int DR, int DS, int DL>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
+    // routed chunks of at most a.lds_rows rows keep their A rows in LDS
+    extern __shared__ __attribute__((aligned(16))) uint16_t a_lds[];
     const int c = blockIdx.y;
     if (c >= *a.nchunks) return;
     const int4 ch = a.chunks[c];
@@ -169,7 +201,41 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const uint16_t* arow = (routed ? a.a_perm : a.a) + src * K + (routed ? kq * 32 : kq * 8);
 
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    if (routed) {
+    if (routed && nrows <= a.lds_rows) {
+        // Stage the chunk's A rows (interleaved copies) in LDS once; the weight
+        // ring then carries only weights and scales, and A comes from LDS.
+        constexpr int D = DL;
+        constexpr int U = D + 1;
+        const int64_t rb = static_cast<int64_t>(group) * (N / 16) + (n >> 4);
+        const uint8_t* q0 = a.wq0 + rb * ng * 1024 + l16 * 64 + kq * 16;
+        const uint8_t* q1 = UP ? a.wq1 + rb * ng * 1024 + l16 * 64 + kq * 16 : nullptr;
+        const float* s0 = a.ws0 + rb * ng * 16 + l16;
+        const float* s1 = UP ? a.ws1 + rb * ng * 16 + l16 : nullptr;
+        WeightSlot sl[U];
+#pragma unroll
+        for (int p = 0; p < D; ++p) load_weights<UP>(sl[p], q0, q1, s0, s1, min(p, ng - 1));
+        const int64_t pitch = K + 8;  // 16-byte pad between rows
+        for (int64_t idx = tid; idx < static_cast<int64_t>(nrows) * (K / 8); idx += NT) {
+            const int r = static_cast<int>(idx / (K / 8));
+            const int64_t col = (idx - r * (K / 8)) * 8;
+            const int64_t srow = UP ? a.perm[row0 + r] / a.top_k : row0 + r;
+            *reinterpret_cast<uint4*>(a_lds + r * pitch + col) =
+                *reinterpret_cast<const uint4*>(a.a_perm + srow * K + col);
+        }
+        __syncthreads();
+        const uint16_t* lrow = a_lds + m * pitch + kq * 32;
+        const int full = ng - ng % U;
+        for (int g0 = 0; g0 < full; g0 += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                load_weights<UP>(sl[(u + D) % U], q0, q1, s0, s1, min(g0 + u + D, ng - 1));
+                compute_lds<UP>(sl[u], lrow, g0 + u, acc0, acc1);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < D; ++u)
+            if (u < ng - full) compute_lds<UP>(sl[u], lrow, full + u, acc0, acc1);
+    } else if (routed) {
         constexpr int D = DR;
         constexpr int U = D + 1;
         // tile row block of this lane's feature; tiles of a row block are consecutive
@@ -231,15 +297,29 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     }
 }
 
-hipError_t launch_decode_up(const DecodeArgs& a, int max_chunks, hipStream_t stream) {
+// LDS budget for staged A rows: 48 KB keeps three blocks (12 waves) per CU
+constexpr int64_t kDecodeLdsBytes = 48 * 1024;
+
+static int lds_rows(int64_t K) {
+    const int64_t r = kDecodeLdsBytes / ((K + 8) * 2);
+    return static_cast<int>(r < kDecodeRows ? r : kDecodeRows);
+}
+
+hipError_t launch_decode_up(const DecodeArgs& args, int max_chunks, hipStream_t stream) {
+    DecodeArgs a = args;
+    a.lds_rows = lds_rows(a.K);
+    const size_t lds = a.lds_rows > 0 ? static_cast<size_t>(a.lds_rows) * (a.K + 8) * 2 : 0;
     dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks));
-    hipLaunchKernelGGL((decode_kernel<true, 3, 1>), grid, dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<true, 3, 1, 7>), grid, dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_down(const DecodeArgs& a, int max_chunks, hipStream_t stream) {
+hipError_t launch_decode_down(const DecodeArgs& args, int max_chunks, hipStream_t stream) {
+    DecodeArgs a = args;
+    a.lds_rows = lds_rows(a.K);
+    const size_t lds = a.lds_rows > 0 ? static_cast<size_t>(a.lds_rows) * (a.K + 8) * 2 : 0;
     dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks));
-    hipLaunchKernelGGL((decode_kernel<false, 3, 2>), grid, dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<false, 3, 2, 7>), grid, dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
 

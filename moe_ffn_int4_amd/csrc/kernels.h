@@ -106,6 +106,7 @@ struct DecodeArgs {
     const uint16_t* sh1;
     uint16_t* h_out;
     float* o_out;
+    int lds_rows;            // set by the launcher: routed chunks this small stage A in LDS
 };
 
 // K7: decode up / down projections over the row chunks
