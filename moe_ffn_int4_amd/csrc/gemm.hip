@@ -1,4 +1,4 @@
-// gemm.hip -- K4/K5/K6: grouped expert GEMMs on gfx950 bf16 MFMA.
+// gemm.hip -- K4/K5/K6: grouped expert GEMMs on gfx950 bf16 MFMA (prefill).
 //
 // Every chosen expert runs its SwiGLU FFN only on the tokens routed to it
 // (discosf.com page "1 卡跑通 Llama 4", section "混合专家路由"), and the
@@ -10,36 +10,46 @@
 //
 // One launch covers all groups: routed experts 0..E-1 (int4 weights, rows =
 // the expert's slots from the dispatch step) and the shared expert as group E
-// (bf16 weights, rows = all T tokens). blockIdx.x walks the row tiles of all
-// groups (tile_base from the dispatch step), blockIdx.y the output columns.
+// (bf16 weights, rows = all T tokens): row tiles of all groups (tile_base from
+// the dispatch step) x column tiles. Block order is XCD-aware: blocks are
+// dealt round-robin to the 8 XCDs, so each XCD is given a contiguous range of
+// tiles, walked in groups of 4 row tiles x all column tiles; the 32 blocks an
+// XCD runs at a time then share the A and B panels of 4 row tiles x 8 column
+// tiles through that XCD's L2 instead of fetching them from HBM again.
 //
 //   up:   H[slot, n]  = silu(A W1^T)[n] * (A W3^T)[n]  (bf16 out)
-//         A = x gathered by slot (routed) or x itself (shared)
-//         a block computes 64 hidden units of W1 and the same 64 of W3, so
-//         the SwiGLU product is formed in registers
+//         A = x gathered by slot (routed) or x itself (shared); a block
+//         computes 128 hidden units of W1 and the same 128 of W3, so the
+//         SwiGLU product is formed in registers
 //   down: O[slot, m]  = (H W2^T)[m]                    (fp32 out)
 //
-// Tiles: 128 rows x 128 columns x 128 reduction (one quantization group) per
-// step, 256 threads = 4 waves in a 2 x 2 grid, each wave 64 x 64 from 4 x 4
-// v_mfma_f32_16x16x32_bf16. A and B are staged through LDS (rows padded by 16
-// bytes so the 16-byte fragment reads are bank-conflict free). Weights come in
-// the tiled layouts (moe_quantize_int4_tiled / moe_pack_bf16_tiled): per step
-// the block reads eight whole 16-row tiles, 1 KB (int4) or 4 KB (bf16) each.
-// Int4 B rows are dequantized on the way into LDS: each thread takes 64 codes
-// of one row (32 bytes), sign-extends the nibbles, multiplies by the group
-// scale in fp32 and rounds to bf16 (round to nearest even). Accumulation is
-// fp32 in the MFMA.
+// Block tile 256 rows x 256 B-rows, reduction step 32 (a quarter of a
+// quantization group); 256 threads = 4 waves in a 2 x 2 grid, each wave 128 x 128 from
+// 8 x 8 v_mfma_f32_16x16x32_bf16 tiles (256 fp32 accumulators per lane). A wave
+// this size reads 1/64 B of LDS per FLOP, half the LDS bandwidth at full MFMA
+// rate. LDS holds two 32 KB stages in a bank-conflict-free fragment order;
+// global data for step k+1 is in flight while step k's MFMAs run (pipeline
+// described at gemm_tile). A partial row tile still runs all its MFMAs on
+// clamped rows (results dropped).
+//
+// Weights come in the tiled layouts (moe_quantize_int4_tiled /
+// moe_pack_bf16_tiled). Int4 B rows are dequantized on the way into LDS:
+// each thread takes 32 codes of one row per step, sign-extends the nibbles,
+// multiplies by the group scale in fp32 and rounds to bf16 (round to nearest
+// even). Accumulation is fp32 in the MFMA.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
 namespace {
-constexpr int BM = kPrefillBM;  // 128 rows (tokens / slots)
-constexpr int BN = 128;         // B rows staged per block (output columns)
-constexpr int BK = kGroup;      // reduction step: one quantization group
-constexpr int LDK = BK + 8;     // LDS row pitch in bf16 elements
+constexpr int BM = kPrefillBM;  // 256 rows (tokens / slots)
+constexpr int BN = 256;         // B rows staged per block
+constexpr int BK = 32;          // reduction step: a quarter of a quantization group
 constexpr int NT = 256;
+static_assert(BM == 256, "tile table row height");
 }  // namespace
 
 struct Tile {
@@ -73,164 +83,226 @@ __device__ __forceinline__ bool find_tile(const GroupedGemmArgs& a, int mt, Tile
     return true;
 }
 
-// 8 int4 codes (one 32-bit word) times scale -> 4 packed bf16 pairs
-__device__ __forceinline__ void dequant8(uint32_t w, float s, uint32_t* out) {
+// 8 int4 codes (one 32-bit word) times scale -> 4 packed bf16 pairs (RNE)
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint32_t o[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        out[j] = pack_bf16x2(static_cast<float>(nib(w, 2 * j)) * s,
-                             static_cast<float>(nib(w, 2 * j + 1)) * s);
+    for (int j = 0; j < 4; ++j) {
+        const bf16x2 v = {static_cast<__bf16>(static_cast<float>(nib(w, 2 * j)) * s),
+                          static_cast<__bf16>(static_cast<float>(nib(w, 2 * j + 1)) * s)};
+        o[j] = __builtin_bit_cast(uint32_t, v);
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-template <bool UP>
-__global__ __launch_bounds__(NT) void grouped_gemm_kernel(GroupedGemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+// One block's tile: ROUTED picks the int4 or bf16 B source at compile time so
+// the reduction loop has no branches (a load under a branch is waited on where
+// the branch joins). Rows past the group's end and B rows past N read a valid
+// clamped address; their results are dropped by the epilogue.
+//
+// LDS holds 2 stages of one 32-wide reduction step: 16 A sub-tiles then
+// 16 B sub-tiles, each 16 rows x 32 k = 1 KB in MFMA fragment order: the
+// 16-byte piece (row n, k 8q..8q+7) sits at slot 16 q + (n ^ c[q]), c = {0, 4,
+// 10, 14}. A fragment read (lane -> n = lane % 16, q = lane / 16) and a staging
+// write (lane -> n = lane / 4, q = lane % 4) then touch distinct banks in every
+// group of 8 or 16 lanes.
+//
+// Step k: the global loads of step k+1 are issued first; each wave then
+// reads all 16 of its fragments of step k from LDS before the first of its 64
+// MFMAs (the reads are forced ahead of the MFMAs, so LDS latency is paid once
+// per step, not once per fragment); then step k+1 goes from registers into
+// the other LDS stage (int4 dequantized on the way); one barrier per step.
+// Loads are not issued under branches: a load under a branch is waited on
+// where the branch joins, which would serialize it with the MFMAs.
+__device__ __forceinline__ int frag_slot(int n, int q) {
+    return (q * 16 + (n ^ ((q * 4) ^ ((q >> 1) * 2)))) * 16;  // bytes in a sub-tile
+}
 
-    Tile tile;
-    if (!find_tile(a, blockIdx.x, tile)) return;
-    const bool routed = tile.group < a.E;
+template <bool UP, bool ROUTED>
+__device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& tile, int nt,
+                                          uint8_t* lds) {
+    constexpr int SUB = 1024;                 // bytes per 16 x 32 sub-tile
+    constexpr int STAGE_BYTES = 32 * SUB;     // 16 A + 16 B sub-tiles
     const int64_t K = a.K, N = a.N;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
-    const int l16 = lane & 15, lq = lane >> 4;
     const int wm = wid >> 1, wn = wid & 1;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * (UP ? BN / 2 : BN);
+    const int64_t n0 = static_cast<int64_t>(nt) * (UP ? BN / 2 : BN);
+    const int64_t ng = K / kGroup;
+    const int steps = static_cast<int>(K / BK);
 
-    // ---- A rows this thread stages: rows (tid + 256 i) / 16, 16-byte column piece (tid & 15)
-    constexpr int AP = BM * BK / 8 / NT;  // 16-byte pieces per thread
+    // ---- A staging: thread -> rows (tid/4) + 64 i, piece q = tid % 4
+    constexpr int AP = BM * BK / 8 / NT;  // 4 pieces per thread
     const uint16_t* arow[AP];
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
-        const int r = (tid + NT * i) >> 4;
-        arow[i] = nullptr;
-        if (r < tile.nrows) {
-            const int64_t s = tile.row0 + r;
-            int64_t src;
-            if (UP) src = routed ? a.perm[s] / a.top_k : s - a.P;
-            else src = s;
-            arow[i] = a.a + src * K + (tid & 15) * 8;
-        }
+        int r = (tid >> 2) + 64 * i;
+        r = r < tile.nrows ? r : tile.nrows - 1;
+        const int64_t s = tile.row0 + r;
+        int64_t src;
+        if (UP) src = ROUTED ? a.perm[s] / a.top_k : s - a.P;
+        else src = s;
+        arow[i] = a.a + src * K + (tid & 3) * 8;
     }
+    // LDS byte offset of this thread's A piece i: sub-tile (tid/64) + 4 i
+    const int a_st = (tid >> 6) * SUB + frag_slot((tid >> 2) & 15, tid & 3);
 
-    // ---- B: LDS row r (0..127) is weight row n0 + (r & 63) of W1 / W3 (up) or
-    // n0 + r of W2 (down). Tiles of one 16-row block are consecutive, ng per block.
-    const int64_t ng = K / kGroup;
-    auto row_block = [&](int r) -> int64_t {  // global 16-row block of LDS row r
-        const int64_t n = UP ? n0 + (r & 63) : n0 + r;
-        return n >> 4;
-    };
-    // int4: thread -> LDS row tid/2, 64 codes (32 bytes) at half (tid & 1)
-    const int qr = tid >> 1, qh = tid & 1;
+    // ---- B staging: B row tid (pieces q = 0..3). Up: rows 0..127 are W1 rows
+    // n0 .. n0+127, rows 128..255 the same rows of W3; down: W2 rows n0+tid
+    // (the last down tile may reach past N: those rows re-read row N-1).
+    int64_t bn = UP ? n0 + (tid & 127) : n0 + tid;
+    bn = bn < N ? bn : N - 1;
     const uint8_t* bq = nullptr;
     const float* bs = nullptr;
-    // bf16: thread -> piece tid of each of the 8 row blocks' 4 KB tiles
-    const uint16_t* bh[8];
-    if (routed) {
-        const int64_t rb = static_cast<int64_t>(tile.group) * (N / 16) + row_block(qr);
-        const uint8_t* q = (UP && qr >= 64) ? a.wq1 : a.wq0;
-        const float* sc = (UP && qr >= 64) ? a.ws1 : a.ws0;
-        bq = q + rb * ng * 1024 + (qr & 15) * 64 + qh * 32;
-        bs = sc + rb * ng * 16 + (qr & 15);
+    const uint16_t* bh = nullptr;
+    if (ROUTED) {
+        const int64_t rb = static_cast<int64_t>(tile.group) * (N / 16) + (bn >> 4);
+        const uint8_t* q = (UP && tid >= 128) ? a.wq1 : a.wq0;
+        const float* sc = (UP && tid >= 128) ? a.ws1 : a.ws0;
+        bq = q + rb * ng * 1024 + (bn & 15) * 64;  // + group * 1024 + quarter * 16
+        bs = sc + rb * ng * 16 + (bn & 15);          // + group * 16
     } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint16_t* src = (UP && i >= 4) ? a.sh1 : a.sh0;
-            bh[i] = src + row_block(i * 16) * ng * 2048 + tid * 8;
-        }
+        const uint16_t* src = (UP && tid >= 128) ? a.sh1 : a.sh0;
+        bh = src + (bn >> 4) * ng * 2048 + (bn & 15) * 32;  // + group*2048 + quarter*512 + 8q
     }
+    const int b_st = 16 * SUB + (tid >> 4) * SUB;  // + frag_slot(tid & 15, q)
 
-    f32x4 acc[4][4];
+    constexpr int BV = ROUTED ? 1 : 4;
+    u32x4 ra[AP], rb[BV];
+    float rs = 0.f;
+    // global -> registers for reduction step k
+    auto load_step = [&](int k) __attribute__((always_inline)) {
+        k = k < steps ? k : steps - 1;  // past the end: reload the last step (unused)
+        const int64_t k0 = static_cast<int64_t>(k) * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // B-fragment row of sub-tile j inside Bs (up: cols 0,1 -> W1 rows, 2,3 -> W3 rows)
-    int brow[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        brow[j] = UP ? ((j < 2) ? wn * 32 + j * 16 : 64 + wn * 32 + (j - 2) * 16) + l16
-                     : wn * 64 + j * 16 + l16;
-
-    for (int64_t g = 0; g < ng; ++g) {
-        const int64_t k0 = g * BK;
-        uint4 av[AP];
-#pragma unroll
-        for (int i = 0; i < AP; ++i)
-            av[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0) : make_uint4(0, 0, 0, 0);
-        uint4 bv[8];
-        float scale = 0.f;
-        if (routed) {
-            bv[0] = *reinterpret_cast<const uint4*>(bq + g * 1024);
-            bv[1] = *reinterpret_cast<const uint4*>(bq + g * 1024 + 16);
-            scale = bs[g * 16];
+        for (int i = 0; i < AP; ++i) ra[i] = *reinterpret_cast<const u32x4*>(arow[i] + k0);
+        const int64_t g = k0 / kGroup;
+        const int quarter = k & 3;
+        if (ROUTED) {
+            rb[0] = *reinterpret_cast<const u32x4*>(bq + g * 1024 + quarter * 16);
+            rs = bs[g * 16];
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) bv[i] = *reinterpret_cast<const uint4*>(bh[i] + g * 2048);
+            for (int c = 0; c < 4; ++c)
+                rb[c] = *reinterpret_cast<const u32x4*>(bh + g * 2048 + quarter * 512 + c * 8);
         }
-        __syncthreads();  // previous step's fragments are consumed
+    };
+    // registers -> LDS stage (int4 B dequantized on the way)
+    auto store_step = [&](int stage) __attribute__((always_inline)) {
+        uint8_t* st = lds + stage * STAGE_BYTES;
 #pragma unroll
-        for (int i = 0; i < AP; ++i) {
-            const int r = (tid + NT * i) >> 4;
-            *reinterpret_cast<uint4*>(&As[r * LDK + (tid & 15) * 8]) = av[i];
+        for (int i = 0; i < AP; ++i) *reinterpret_cast<u32x4*>(st + a_st + 4 * i * SUB) = ra[i];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 v = ROUTED ? dequant8(rb[0][q], rs) : rb[ROUTED ? 0 : q];
+            *reinterpret_cast<u32x4*>(st + b_st + frag_slot(tid & 15, q)) = v;
         }
-        if (routed) {
-            uint32_t d[32];
-            const uint32_t w[8] = {bv[0].x, bv[0].y, bv[0].z, bv[0].w, bv[1].x, bv[1].y, bv[1].z, bv[1].w};
+    };
+
+    f32x4 acc[8][8];
+
+    // fragment read offsets: lane's slot, this wave's A and B sub-tiles
+    const int lslot = frag_slot(lane & 15, lane >> 4);
+    int a_off[8], b_off[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) dequant8(w[i], scale, d + 4 * i);
-            uint4* dst = reinterpret_cast<uint4*>(&Bs[qr * LDK + qh * 64]);
+    for (int i = 0; i < 8; ++i) a_off[i] = (wm * 8 + i) * SUB + lslot;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) dst[i] = make_uint4(d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]);
-        } else {
-            // piece tid of a step-major tile: step tid/64, row (tid/4)%16, columns 8*(tid%4)
-            const int step = tid >> 6, row = (tid >> 2) & 15, col = step * 32 + (tid & 3) * 8;
+    for (int j = 0; j < 8; ++j)
+        b_off[j] = 16 * SUB + lslot +
+                   SUB * (UP ? ((j < 4) ? wn * 4 + j : 8 + wn * 4 + (j - 4)) : wn * 8 + j);
+
+    // FIRST: the accumulators start from the MFMA's zero operand (no separate
+    // zeroing of 256 registers, which also keeps the register allocation of the
+    // loop-carried accumulators stable)
+    auto mfma_step = [&](int stage, auto first) __attribute__((always_inline)) {
+        constexpr bool FIRST = decltype(first)::value;
+        const uint8_t* st = lds + stage * STAGE_BYTES;
+        bf16x8 fa[8], fb[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<uint4*>(&Bs[(i * 16 + row) * LDK + col]) = bv[i];
-        }
+        for (int j = 0; j < 8; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(st + b_off[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    fa[i], fb[j], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i][j], 0, 0, 0);
+        // scheduling groups: the 16 LDS reads, then the 64 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);
+    };
+
+    load_step(0);
+    store_step(0);
+    __syncthreads();
+    load_step(1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(0, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    store_step(1);
+    __syncthreads();
+    for (int k = 1; k < steps; ++k) {
+        load_step(k + 1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+        mfma_step(k & 1, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);  // stores (which wait for the loads) after the MFMAs
+        store_step((k & 1) ^ 1);
         __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8 af[4], bf[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + i * 16 + l16) * LDK + kk + lq * 8]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = *reinterpret_cast<const bf16x8*>(&Bs[brow[j] * LDK + kk + lq * 8]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
     }
 
     // ---- epilogue: D[row][col], row = 4 * lq + r inside a 16 x 16 sub-tile, col = l16
+    const int l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = wm * 64 + i * 16 + lq * 4 + r;
+            const int row = wm * 128 + i * 16 + lq * 4 + r;
             if (row >= tile.nrows) continue;
             const int64_t orow = tile.row0 + row;
             if (UP) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float g = acc[i][j][r], u = acc[i][j + 2][r];
-                    const int64_t col = n0 + wn * 32 + j * 16 + l16;
+                for (int j = 0; j < 4; ++j) {
+                    const float g = acc[i][j][r], u = acc[i][j + 4][r];
+                    const int64_t col = n0 + wn * 64 + j * 16 + l16;
                     a.h_out[orow * N + col] = f32_to_bf16(siluf_(g) * u);
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t col = n0 + wn * 64 + j * 16 + l16;
-                    a.o_out[orow * N + col] = acc[i][j][r];
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t col = n0 + wn * 128 + j * 16 + l16;
+                    if (col < N) a.o_out[orow * N + col] = acc[i][j][r];
                 }
             }
         }
     }
+}
+
+template <bool UP>
+__global__ __launch_bounds__(NT) void grouped_gemm_kernel(GroupedGemmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 3 stages of [A | B]
+
+    // ---- block -> (row tile, column tile), XCD-aware (see the file comment)
+    const int ncol = static_cast<int>(UP ? a.N / (BN / 2) : (a.N + BN - 1) / BN);
+    const int nrow = a.tile_base[a.E + 1];
+    const int total = nrow * ncol;
+    const int L = blockIdx.x;
+    if (L >= total) return;
+    constexpr int kXcd = 8, kGroupRows = 4;
+    const int xcd = L % kXcd, slot = L / kXcd;
+    const int base = total / kXcd, extra = total % kXcd;
+    const int lin = xcd * base + (xcd < extra ? xcd : extra) + slot;  // XCD-contiguous order
+    const int span = kGroupRows * ncol;
+    const int first_row = (lin / span) * kGroupRows;
+    const int rows_here = nrow - first_row < kGroupRows ? nrow - first_row : kGroupRows;
+    const int mt = first_row + (lin % span) % rows_here;
+    const int nt = (lin % span) / rows_here;
+
+    Tile tile;
+    if (!find_tile(a, mt, tile)) return;
+    if (tile.group < a.E) gemm_tile<UP, true>(a, tile, nt, lds);
+    else gemm_tile<UP, false>(a, tile, nt, lds);
 }
 
 static unsigned max_row_tiles(const GroupedGemmArgs& a) {
@@ -239,15 +311,28 @@ static unsigned max_row_tiles(const GroupedGemmArgs& a) {
     return static_cast<unsigned>((a.P + BM - 1) / BM + e_bound + (a.T + BM - 1) / BM);
 }
 
+static constexpr size_t kGemmLds = 2 * 32 * 1024;  // 2 stages of 16 A + 16 B sub-tiles
+
+// more than 64 KB of dynamic LDS must be allowed per kernel once
+template <bool UP>
+static hipError_t allow_lds() {
+    static hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<UP>),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                                              static_cast<int>(kGemmLds));
+    return e;
+}
+
 hipError_t launch_grouped_up(const GroupedGemmArgs& a, hipStream_t stream) {
-    dim3 grid(max_row_tiles(a), static_cast<unsigned>(a.N / (BN / 2)));
-    hipLaunchKernelGGL(grouped_gemm_kernel<true>, grid, dim3(NT), 0, stream, a);
+    if (hipError_t e = allow_lds<true>(); e != hipSuccess) return e;
+    dim3 grid(max_row_tiles(a) * static_cast<unsigned>(a.N / (BN / 2)));
+    hipLaunchKernelGGL(grouped_gemm_kernel<true>, grid, dim3(NT), kGemmLds, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_down(const GroupedGemmArgs& a, hipStream_t stream) {
-    dim3 grid(max_row_tiles(a), static_cast<unsigned>(a.N / BN));
-    hipLaunchKernelGGL(grouped_gemm_kernel<false>, grid, dim3(NT), 0, stream, a);
+    if (hipError_t e = allow_lds<false>(); e != hipSuccess) return e;
+    dim3 grid(max_row_tiles(a) * static_cast<unsigned>((a.N + BN - 1) / BN));
+    hipLaunchKernelGGL(grouped_gemm_kernel<false>, grid, dim3(NT), kGemmLds, stream, a);
     return hipGetLastError();
 }
 

@@ -49,6 +49,8 @@ SMALL = {
     "one expert": W.config(0).with_(T=130, E=1, top_k=1),
     "tile edge 128": W.config(0).with_(T=128, E=2, top_k=1),
     "tile edge 129": W.config(0).with_(T=129, E=2, top_k=1),
+    "tile edge 256": W.config(0).with_(T=256, E=1, top_k=1),
+    "tile edge 257": W.config(0).with_(T=257, E=2, d=384, top_k=1),
     "multi-block routing": W.config(0).with_(T=600, E=16, h=384, top_k=2),
     "k=16 of 40": W.config(0).with_(T=40, d=512, E=40, h=256, top_k=16),
 }
