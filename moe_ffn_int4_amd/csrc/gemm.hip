@@ -13,8 +13,8 @@
 // (bf16 weights, rows = all T tokens): row tiles of all groups (tile_base from
 // the dispatch step) x column tiles. Block order is XCD-aware: blocks are
 // dealt round-robin to the 8 XCDs, so each XCD is given a contiguous range of
-// tiles, walked in groups of 4 row tiles x all column tiles; the 32 blocks an
-// XCD runs at a time then share the A and B panels of 4 row tiles x 8 column
+// tiles, walked in groups of 8 row tiles x all column tiles; the 64 blocks an
+// XCD runs at a time then share the A and B panels of 8 row tiles x 8 column
 // tiles through that XCD's L2 instead of fetching them from HBM again.
 //
 //   up:   H[slot, n]  = silu(A W1^T)[n] * (A W3^T)[n]  (bf16 out)
@@ -23,14 +23,15 @@
 //         SwiGLU product is formed in registers
 //   down: O[slot, m]  = (H W2^T)[m]                    (fp32 out)
 //
-// Block tile 256 rows x 256 B-rows, reduction step 32 (a quarter of a
-// quantization group); 256 threads = 4 waves in a 2 x 2 grid, each wave 128 x 128 from
-// 8 x 8 v_mfma_f32_16x16x32_bf16 tiles (256 fp32 accumulators per lane). A wave
-// this size reads 1/64 B of LDS per FLOP, half the LDS bandwidth at full MFMA
-// rate. LDS holds two 32 KB stages in a bank-conflict-free fragment order;
-// global data for step k+1 is in flight while step k's MFMAs run (pipeline
-// described at gemm_tile). A partial row tile still runs all its MFMAs on
-// clamped rows (results dropped).
+// Block tile 128 rows x 256 B-rows, reduction step 32 (a quarter of a
+// quantization group); 256 threads = 4 waves in a 2 x 2 grid, each wave 64 x
+// 128 from 4 x 8 v_mfma_f32_16x16x32_bf16 tiles (128 fp32 accumulators per
+// lane). That leaves room for two blocks per CU (two waves per SIMD, 2 x 48 KB
+// of LDS): with one wave per SIMD nothing covers a wave's wait for global or
+// LDS data, with two the other block's MFMAs do. LDS holds two 24 KB stages in
+// a bank-conflict-free fragment order; global data for step k+1 is in flight
+// while step k's MFMAs run (pipeline described at gemm_tile). A partial row
+// tile still runs all its MFMAs on clamped rows (results dropped).
 //
 // Weights come in the tiled layouts (moe_quantize_int4_tiled /
 // moe_pack_bf16_tiled). Int4 B rows are dequantized on the way into LDS:
@@ -45,11 +46,11 @@
 namespace moe {
 
 namespace {
-constexpr int BM = kPrefillBM;  // 256 rows (tokens / slots)
+constexpr int BM = kPrefillBM;  // 128 rows (tokens / slots)
 constexpr int BN = 256;         // B rows staged per block
 constexpr int BK = 32;          // reduction step: a quarter of a quantization group
 constexpr int NT = 256;
-static_assert(BM == 256, "tile table row height");
+static_assert(BM == 128, "tile table row height");
 }  // namespace
 
 struct Tile {
@@ -123,7 +124,8 @@ template <bool UP, bool ROUTED>
 __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& tile, int nt,
                                           uint8_t* lds) {
     constexpr int SUB = 1024;                 // bytes per 16 x 32 sub-tile
-    constexpr int STAGE_BYTES = 32 * SUB;     // 16 A + 16 B sub-tiles
+    constexpr int ASUB = BM / 16;             // 8 A sub-tiles
+    constexpr int STAGE_BYTES = (ASUB + 16) * SUB;  // 8 A + 16 B sub-tiles
     const int64_t K = a.K, N = a.N;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
@@ -133,7 +135,7 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
     const int steps = static_cast<int>(K / BK);
 
     // ---- A staging: thread -> rows (tid/4) + 64 i, piece q = tid % 4
-    constexpr int AP = BM * BK / 8 / NT;  // 4 pieces per thread
+    constexpr int AP = BM * BK / 8 / NT;  // 2 pieces per thread
     const uint16_t* arow[AP];
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
@@ -166,7 +168,7 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         const uint16_t* src = (UP && tid >= 128) ? a.sh1 : a.sh0;
         bh = src + (bn >> 4) * ng * 2048 + (bn & 15) * 32;  // + group*2048 + quarter*512 + 8q
     }
-    const int b_st = 16 * SUB + (tid >> 4) * SUB;  // + frag_slot(tid & 15, q)
+    const int b_st = ASUB * SUB + (tid >> 4) * SUB;  // + frag_slot(tid & 15, q)
 
     constexpr int BV = ROUTED ? 1 : 4;
     u32x4 ra[AP], rb[BV];
@@ -200,16 +202,16 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         }
     };
 
-    f32x4 acc[8][8];
+    f32x4 acc[4][8];
 
     // fragment read offsets: lane's slot, this wave's A and B sub-tiles
     const int lslot = frag_slot(lane & 15, lane >> 4);
-    int a_off[8], b_off[8];
+    int a_off[4], b_off[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a_off[i] = (wm * 8 + i) * SUB + lslot;
+    for (int i = 0; i < 4; ++i) a_off[i] = (wm * 4 + i) * SUB + lslot;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        b_off[j] = 16 * SUB + lslot +
+        b_off[j] = ASUB * SUB + lslot +
                    SUB * (UP ? ((j < 4) ? wn * 4 + j : 8 + wn * 4 + (j - 4)) : wn * 8 + j);
 
     // FIRST: the accumulators start from the MFMA's zero operand (no separate
@@ -218,20 +220,20 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
     auto mfma_step = [&](int stage, auto first) __attribute__((always_inline)) {
         constexpr bool FIRST = decltype(first)::value;
         const uint8_t* st = lds + stage * STAGE_BYTES;
-        bf16x8 fa[8], fb[8];
+        bf16x8 fa[4], fb[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(st + b_off[j]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i]);
+        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     fa[i], fb[j], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i][j], 0, 0, 0);
-        // scheduling groups: the 16 LDS reads, then the 64 MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);
+        // scheduling groups: the 12 LDS reads, then the 32 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
     };
 
     load_step(0);
@@ -255,10 +257,10 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
     // ---- epilogue: D[row][col], row = 4 * lq + r inside a 16 x 16 sub-tile, col = l16
     const int l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = wm * 128 + i * 16 + lq * 4 + r;
+            const int row = wm * 64 + i * 16 + lq * 4 + r;
             if (row >= tile.nrows) continue;
             const int64_t orow = tile.row0 + row;
             if (UP) {
@@ -280,7 +282,7 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
 }
 
 template <bool UP>
-__global__ __launch_bounds__(NT) void grouped_gemm_kernel(GroupedGemmArgs a) {
+__global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(GroupedGemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 3 stages of [A | B]
 
     // ---- block -> (row tile, column tile), XCD-aware (see the file comment)
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GroupedGemmArgs a) {
     const int total = nrow * ncol;
     const int L = blockIdx.x;
     if (L >= total) return;
-    constexpr int kXcd = 8, kGroupRows = 4;
+    constexpr int kXcd = 8, kGroupRows = 8;
     const int xcd = L % kXcd, slot = L / kXcd;
     const int base = total / kXcd, extra = total % kXcd;
     const int lin = xcd * base + (xcd < extra ? xcd : extra) + slot;  // XCD-contiguous order
@@ -311,7 +313,7 @@ static unsigned max_row_tiles(const GroupedGemmArgs& a) {
     return static_cast<unsigned>((a.P + BM - 1) / BM + e_bound + (a.T + BM - 1) / BM);
 }
 
-static constexpr size_t kGemmLds = 2 * 32 * 1024;  // 2 stages of 16 A + 16 B sub-tiles
+static constexpr size_t kGemmLds = 2 * 24 * 1024;  // 2 stages of 8 A + 16 B sub-tiles
 
 // more than 64 KB of dynamic LDS must be allowed per kernel once
 template <bool UP>

@@ -14,7 +14,7 @@ constexpr int kMaxExperts = 256;
 
 // Tile height (token rows) of the prefill grouped GEMMs; the dispatch step
 // lays out its tile table for this height.
-constexpr int kPrefillBM = 256;
+constexpr int kPrefillBM = 128;
 
 // Rows per decode chunk (the M of one MFMA tile).
 constexpr int kDecodeRows = 16;
