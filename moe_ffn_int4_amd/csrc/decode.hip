@@ -177,15 +177,27 @@ template <bool UP, int DR, int DS, int DL>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     // routed chunks of at most a.lds_rows rows keep their A rows in LDS
     extern __shared__ __attribute__((aligned(16))) uint16_t a_lds[];
-    const int c = blockIdx.y;
+    // Rows 0 .. max_chunks-1 of the grid take the chunks; the shared expert's
+    // chunks (listed first) get three more rows each (max_chunks + 3 c + s - 1):
+    // shared sub-block s = 0..3 of a 64-feature range covers its 16 features
+    // s*16 .. s*16+15 with all four waves, each wave a quarter of the reduction.
+    // Shared chunks stream bf16 weights (4x the bytes of an int4 chunk); split
+    // this way they spread over four times as many blocks and CUs.
+    int c = blockIdx.y, sub = 0;
+    if (c >= a.max_chunks) {
+        const int e = c - a.max_chunks;
+        c = e / 3;
+        sub = 1 + e % 3;
+    }
     if (c >= *a.nchunks) return;
     const int4 ch = a.chunks[c];
     const int group = ch.x, row0 = ch.y, nrows = ch.z;
     const bool routed = group < a.E;
+    if (routed && blockIdx.y >= a.max_chunks) return;
     const int64_t K = a.K, N = a.N;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kq = lane >> 4;
-    const int64_t n = static_cast<int64_t>(blockIdx.x) * 64 + wave * 16 + l16;  // B column
+    const int64_t n = static_cast<int64_t>(blockIdx.x) * 64 + (routed ? wave : sub) * 16 + l16;  // B column
     const int ng = static_cast<int>(K / kGroup);
 
     // A row of MFMA row l16: routed experts read the interleaved copy, the shared
@@ -263,25 +275,51 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         for (int u = 0; u < D; ++u)
             if (u < ng - full) compute_routed<UP>(sl[u], acc0, acc1);
     } else {
+        // this wave's quarter of the groups: gb .. gb + cnt - 1 (cnt may be 0)
         constexpr int D = DS;
         constexpr int U = D + 1;
+        const int gb = (wave * ng) / 4;
+        const int cnt = ((wave + 1) * ng) / 4 - gb;
+        const int last = cnt > 0 ? cnt - 1 : 0;
         const int64_t rb = n >> 4;
-        const uint16_t* h0 = a.sh0 + rb * ng * 2048 + l16 * 32 + kq * 8;
-        const uint16_t* h1 = UP ? a.sh1 + rb * ng * 2048 + l16 * 32 + kq * 8 : nullptr;
+        const uint16_t* h0 = a.sh0 + rb * ng * 2048 + l16 * 32 + kq * 8 + gb * 2048;
+        const uint16_t* h1 = UP ? a.sh1 + rb * ng * 2048 + l16 * 32 + kq * 8 + gb * 2048 : nullptr;
+        const uint16_t* ar = arow + gb * kGroup;
         SharedSlot sl[U];
 #pragma unroll
-        for (int p = 0; p < D; ++p) load_shared<UP>(sl[p], h0, h1, arow, min(p, ng - 1));
-        const int full = ng - ng % U;
+        for (int p = 0; p < D; ++p) load_shared<UP>(sl[p], h0, h1, ar, min(p, last));
+        const int full = cnt - cnt % U;
         for (int g0 = 0; g0 < full; g0 += U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                load_shared<UP>(sl[(u + D) % U], h0, h1, arow, min(g0 + u + D, ng - 1));
+                load_shared<UP>(sl[(u + D) % U], h0, h1, ar, min(g0 + u + D, last));
                 compute_shared<UP>(sl[u], acc0, acc1);
             }
         }
 #pragma unroll
         for (int u = 0; u < D; ++u)
-            if (u < ng - full) compute_shared<UP>(sl[u], acc0, acc1);
+            if (u < cnt - full) compute_shared<UP>(sl[u], acc0, acc1);
+        // sum the four waves' partial accumulators in wave order (8 KB of LDS)
+        float* red = reinterpret_cast<float*>(a_lds);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            red[(wave * 64 + lane) * 8 + r] = acc0[r];
+            red[(wave * 64 + lane) * 8 + 4 + r] = acc1[r];
+        }
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            acc0[r] = red[lane * 8 + r];
+            acc1[r] = red[lane * 8 + 4 + r];
+        }
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc0[r] += red[(w * 64 + lane) * 8 + r];
+                acc1[r] += red[(w * 64 + lane) * 8 + 4 + r];
+            }
     }
 
     // D[m][n]: m = 4 * kq + r (token row of the chunk), n = l16 (this lane's feature)
@@ -299,28 +337,33 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 
 // LDS budget for staged A rows: 48 KB keeps three blocks (12 waves) per CU
 constexpr int64_t kDecodeLdsBytes = 48 * 1024;
+constexpr size_t kReduceLdsBytes = 4 * 64 * 8 * sizeof(float);  // shared-chunk wave sums
 
 static int lds_rows(int64_t K) {
     const int64_t r = kDecodeLdsBytes / ((K + 8) * 2);
     return static_cast<int>(r < kDecodeRows ? r : kDecodeRows);
 }
 
-hipError_t launch_decode_up(const DecodeArgs& args, int max_chunks, hipStream_t stream) {
+// grid: N / 64 feature ranges x (chunks + 3 extra rows per shared-expert chunk)
+template <bool UP, int DR, int DS, int DL>
+static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, hipStream_t stream) {
     DecodeArgs a = args;
     a.lds_rows = lds_rows(a.K);
-    const size_t lds = a.lds_rows > 0 ? static_cast<size_t>(a.lds_rows) * (a.K + 8) * 2 : 0;
-    dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks));
-    hipLaunchKernelGGL((decode_kernel<true, 3, 1, 7>), grid, dim3(NT), lds, stream, a);
+    a.max_chunks = max_chunks;
+    size_t lds = a.lds_rows > 0 ? static_cast<size_t>(a.lds_rows) * (a.K + 8) * 2 : 0;
+    lds = lds > kReduceLdsBytes ? lds : kReduceLdsBytes;
+    const int64_t shared_chunks = (a.T + kDecodeRows - 1) / kDecodeRows;
+    dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks + 3 * shared_chunks));
+    hipLaunchKernelGGL((decode_kernel<UP, DR, DS, DL>), grid, dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
 
+hipError_t launch_decode_up(const DecodeArgs& args, int max_chunks, hipStream_t stream) {
+    return launch_decode<true, 3, 1, 7>(args, max_chunks, stream);
+}
+
 hipError_t launch_decode_down(const DecodeArgs& args, int max_chunks, hipStream_t stream) {
-    DecodeArgs a = args;
-    a.lds_rows = lds_rows(a.K);
-    const size_t lds = a.lds_rows > 0 ? static_cast<size_t>(a.lds_rows) * (a.K + 8) * 2 : 0;
-    dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks));
-    hipLaunchKernelGGL((decode_kernel<false, 3, 2, 7>), grid, dim3(NT), lds, stream, a);
-    return hipGetLastError();
+    return launch_decode<false, 3, 2, 7>(args, max_chunks, stream);
 }
 
 }  // namespace moe

@@ -107,6 +107,7 @@ struct DecodeArgs {
     uint16_t* h_out;
     float* o_out;
     int lds_rows;            // set by the launcher: routed chunks this small stage A in LDS
+    int max_chunks;          // set by the launcher: grid rows of the chunk list
 };
 
 // K7: decode up / down projections over the row chunks
