@@ -61,7 +61,7 @@ def parse():
     return ap.parse_args()
 
 
-STAGE_TRAFFIC_KEY = {"decode_up": "decode_up"}
+STAGE_TRAFFIC_KEY = {"decode_up": "decode_up", "grouped_up": "grouped_up"}
 
 
 def measured_traffic(stage: str, workload: str):
