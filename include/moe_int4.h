@@ -49,9 +49,14 @@ enum moe_status {
 };
 
 enum moe_path {
-    MOE_PATH_AUTO = 0,     /* decode path for small batches, prefill otherwise */
-    MOE_PATH_PREFILL = 1,  /* grouped int4 GEMMs on MFMA */
-    MOE_PATH_DECODE = 2    /* HBM-streaming GEMV over the touched experts */
+    MOE_PATH_AUTO = 0,     /* DECODE for at most 64 token-expert pairs; HYBRID when the
+                              pairs average under 256 per routed expert; PREFILL otherwise */
+    MOE_PATH_PREFILL = 1,  /* grouped int4 GEMMs on MFMA for every expert */
+    MOE_PATH_DECODE = 2,   /* HBM-streaming GEMV over the touched experts */
+    MOE_PATH_HYBRID = 3    /* grouped GEMMs for the shared expert and for routed experts with
+                              more than 32 pairs; routed experts with 1..32 pairs on the
+                              streaming kernel, which reads their weights once instead of
+                              padding them to 128-row GEMM tiles */
 };
 
 /* Limits checked by validation. */

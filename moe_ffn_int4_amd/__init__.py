@@ -28,7 +28,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_int4.so")
 GROUP = 128
-PATHS = {"auto": 0, "prefill": 1, "decode": 2}
+PATHS = {"auto": 0, "prefill": 1, "decode": 2, "hybrid": 3}
 
 MOE_OK = 0
 

@@ -93,8 +93,12 @@ bool small_routing(const moe_dims& d) {
     return d.T * d.E <= moe::kSmallRouteLogits && d.T * d.top_k <= moe::kSmallRoutePairs;
 }
 
-// MOE_PATH_AUTO: the streaming decode path for small batches.
+// MOE_PATH_AUTO: the streaming decode path for small batches; the hybrid path
+// when the pairs average under kHybridAvgPairs per routed expert.
 constexpr int64_t kDecodeMaxPairs = 64;
+constexpr int64_t kHybridAvgPairs = 256;
+// MOE_PATH_HYBRID: routed experts with at most this many pairs stream
+constexpr int kHybridRows = 32;
 
 int check_dims(const moe_dims* d) {
     if (!d) return fail(MOE_ERR_INVALID_ARG, "dims is NULL");
@@ -257,9 +261,10 @@ Routing carve(const moe_dims& d, void* ws) {
 
 // Router partial logits, then either the one-block small-batch finish (top-k,
 // dispatch, decode chunks) or the top-k kernel + the per-expert dispatch kernel.
+// small_rows: which groups get streaming chunks and which GEMM tiles (build_work_lists)
 int run_routing(const moe_dims& d, const uint16_t* x, const float* wr, const float* b,
                 const Routing& R, int32_t* ids_out, float* gates_out, uint16_t* x_perm,
-                hipStream_t s) {
+                int small_rows, hipStream_t s) {
     const moe::RouterPlan plan = moe::router_plan(d.T, d.d, d.E);
     CHECK(timed(MOE_STAGE_ROUTER, s, "router launch", [&] {
         return moe::launch_router_partials(x, wr, d.T, d.d, d.E, plan, R.partials, x_perm, s);
@@ -267,7 +272,7 @@ int run_routing(const moe_dims& d, const uint16_t* x, const float* wr, const flo
     if (small_routing(d)) {
         CHECK(timed(MOE_STAGE_TOPK, s, "small routing launch", [&] {
             return moe::launch_route_small(R.partials, plan.slices, b, d.T, d.E, d.top_k,
-                                           moe::kPrefillBM, R.logits, R.ids, R.gates, ids_out,
+                                           moe::kPrefillBM, small_rows, R.logits, R.ids, R.gates, ids_out,
                                            gates_out, R.counts, R.offsets, R.tile_base, R.perm,
                                            R.inv, R.chunks, R.nchunks, s);
         }));
@@ -278,7 +283,7 @@ int run_routing(const moe_dims& d, const uint16_t* x, const float* wr, const flo
                                 R.gates, ids_out, gates_out, s);
     }));
     CHECK(timed(MOE_STAGE_DISPATCH, s, "dispatch launch", [&] {
-        return moe::launch_dispatch(R.ids, d.T, d.top_k, d.E, moe::kPrefillBM, R.counts, R.offsets,
+        return moe::launch_dispatch(R.ids, d.T, d.top_k, d.E, moe::kPrefillBM, small_rows, R.counts, R.offsets,
                                     R.tile_base, R.perm, R.inv, R.chunks, R.nchunks, s);
     }));
     return MOE_OK;
@@ -385,7 +390,7 @@ int moe_route(const moe_dims* dims, const uint16_t* x, const float* router_w,
     const moe_dims& d = *dims;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Routing R = carve(d, workspace);
-    CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates, nullptr, s));
+    CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates, nullptr, 0, s));
     const size_t P = static_cast<size_t>(d.T) * d.top_k;
     if (logits)
         HIP_CHECK(hipMemcpyAsync(logits, R.logits, d.T * d.E * 4, hipMemcpyDeviceToDevice, s), "copy");
@@ -417,7 +422,8 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
     CHECK(check_ptr(y, "y"));
     if (topk_ids) CHECK(check_ptr(topk_ids, "topk_ids", 4));
     if (topk_gates) CHECK(check_ptr(topk_gates, "topk_gates", 4));
-    if (path != MOE_PATH_AUTO && path != MOE_PATH_PREFILL && path != MOE_PATH_DECODE)
+    if (path != MOE_PATH_AUTO && path != MOE_PATH_PREFILL && path != MOE_PATH_DECODE &&
+        path != MOE_PATH_HYBRID)
         return fail(MOE_ERR_INVALID_ARG, "path %d unknown", path);
     CHECK(device_ok());
 
@@ -432,10 +438,16 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
 
     const bool decode =
         path == MOE_PATH_DECODE || (path == MOE_PATH_AUTO && P <= kDecodeMaxPairs);
+    const bool hybrid = !decode && (path == MOE_PATH_HYBRID ||
+                                    (path == MOE_PATH_AUTO && P < kHybridAvgPairs * d.E));
+    const int small_rows = decode ? -1 : (hybrid ? kHybridRows : 0);
     uint16_t* x_perm = reinterpret_cast<uint16_t*>(base + L.x_perm);
-    CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates, decode ? x_perm : nullptr, s));
+    CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates,
+                      decode || hybrid ? x_perm : nullptr, small_rows, s));
 
-    if (decode) {
+    // streaming projections over the chunk list: every group (decode path) or
+    // the small routed experts (hybrid path)
+    auto stream_up = [&](int max_chunks, int shared_chunks) {
         moe::DecodeArgs a{};
         a.T = d.T;
         a.P = P;
@@ -455,22 +467,37 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
         a.sh0 = sh->s1;
         a.sh1 = sh->s3;
         a.h_out = H;
-        CHECK(timed(MOE_STAGE_DECODE_UP, s, "decode up launch",
-                    [&] { return moe::launch_decode_up(a, L.max_chunks, s); }));
+        return timed(MOE_STAGE_DECODE_UP, s, "decode up launch",
+                     [&] { return moe::launch_decode_up(a, max_chunks, shared_chunks, s); });
+    };
+    auto stream_down = [&](int max_chunks, int shared_chunks) {
+        moe::DecodeArgs a{};
+        a.T = d.T;
+        a.P = P;
+        a.top_k = d.top_k;
+        a.E = static_cast<int>(d.E);
+        a.perm = R.perm;
+        a.chunks = R.chunks;
+        a.nchunks = R.nchunks;
         a.a = H;
-        a.a_perm = H;  // routed rows of H were written interleaved by the up projection
+        a.a_perm = H;  // routed rows of H were written interleaved by the streaming up projection
         a.K = d.h;
         a.N = d.d;
         a.wq0 = ex->w2q;
         a.ws0 = ex->w2s;
-        a.wq1 = nullptr;
-        a.ws1 = nullptr;
         a.sh0 = sh->s2;
-        a.sh1 = nullptr;
-        a.h_out = nullptr;
         a.o_out = O;
-        CHECK(timed(MOE_STAGE_DECODE_DOWN, s, "decode down launch",
-                    [&] { return moe::launch_decode_down(a, L.max_chunks, s); }));
+        return timed(MOE_STAGE_DECODE_DOWN, s, "decode down launch",
+                     [&] { return moe::launch_decode_down(a, max_chunks, shared_chunks, s); });
+    };
+    // hybrid: at most min(E, P) small experts of at most two 16-row chunks each
+    const int64_t hybrid_chunks =
+        (d.E < P ? d.E : P) * ((kHybridRows + moe::kDecodeRows - 1) / moe::kDecodeRows);
+
+    if (decode) {
+        const int shared_chunks = static_cast<int>((d.T + moe::kDecodeRows - 1) / moe::kDecodeRows);
+        CHECK(stream_up(L.max_chunks, shared_chunks));
+        CHECK(stream_down(L.max_chunks, shared_chunks));
     } else {
         moe::GroupedGemmArgs g{};
         g.T = d.T;
@@ -493,6 +520,7 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
         g.sh1 = sh->s3;
         g.h_out = H;
         CHECK(timed(MOE_STAGE_UP, s, "grouped up launch", [&] { return moe::launch_grouped_up(g, s); }));
+        if (hybrid) CHECK(stream_up(static_cast<int>(hybrid_chunks), 0));
 
         g.a = H;
         g.K = d.h;
@@ -507,6 +535,7 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
         g.o_out = O;
         CHECK(timed(MOE_STAGE_DOWN, s, "grouped down launch",
                     [&] { return moe::launch_grouped_down(g, s); }));
+        if (hybrid) CHECK(stream_down(static_cast<int>(hybrid_chunks), 0));
     }
 
     CHECK(timed(MOE_STAGE_COMBINE, s, "combine launch", [&] {

@@ -344,26 +344,30 @@ static int lds_rows(int64_t K) {
     return static_cast<int>(r < kDecodeRows ? r : kDecodeRows);
 }
 
-// grid: N / 64 feature ranges x (chunks + 3 extra rows per shared-expert chunk)
+// grid: N / 64 feature ranges x (chunks + 3 extra rows per shared-expert chunk);
+// max_chunks bounds the chunk list, shared_chunks is the number of shared-expert
+// chunks at its head (0 when the shared expert runs on the GEMMs)
 template <bool UP, int DR, int DS, int DL>
-static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, hipStream_t stream) {
+static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, int shared_chunks,
+                                hipStream_t stream) {
     DecodeArgs a = args;
     a.lds_rows = lds_rows(a.K);
     a.max_chunks = max_chunks;
     size_t lds = a.lds_rows > 0 ? static_cast<size_t>(a.lds_rows) * (a.K + 8) * 2 : 0;
     lds = lds > kReduceLdsBytes ? lds : kReduceLdsBytes;
-    const int64_t shared_chunks = (a.T + kDecodeRows - 1) / kDecodeRows;
     dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks + 3 * shared_chunks));
     hipLaunchKernelGGL((decode_kernel<UP, DR, DS, DL>), grid, dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_up(const DecodeArgs& args, int max_chunks, hipStream_t stream) {
-    return launch_decode<true, 3, 1, 7>(args, max_chunks, stream);
+hipError_t launch_decode_up(const DecodeArgs& args, int max_chunks, int shared_chunks,
+                            hipStream_t stream) {
+    return launch_decode<true, 3, 1, 7>(args, max_chunks, shared_chunks, stream);
 }
 
-hipError_t launch_decode_down(const DecodeArgs& args, int max_chunks, hipStream_t stream) {
-    return launch_decode<false, 3, 2, 7>(args, max_chunks, stream);
+hipError_t launch_decode_down(const DecodeArgs& args, int max_chunks, int shared_chunks,
+                              hipStream_t stream) {
+    return launch_decode<false, 3, 2, 7>(args, max_chunks, shared_chunks, stream);
 }
 
 }  // namespace moe

@@ -12,8 +12,9 @@
 //   tile_base[g] first GEMM row-tile of group g for tiles of `tile_rows`
 //                rows: routed experts are groups 0..E-1, the shared expert
 //                (all T tokens) is group E; tile_base[E+1] = total tiles.
-//   chunks       the decode path's row chunks (group, first row, rows) of at
-//                most kDecodeRows rows, and their number in *nchunks.
+//   chunks       row chunks (group, first row, rows) of at most kDecodeRows
+//                rows for the streaming kernel, and their number in *nchunks
+//                (which groups are chunked and which tiled: build_work_lists)
 // One block per expert. Each block histograms all P ids in LDS, scans, and
 // compacts the pairs of its own expert: every thread owns a contiguous segment
 // of pairs, counts its matches, takes its base from a block-wide exclusive
@@ -21,6 +22,7 @@
 // whatever order the atomics land in. Integer work, a few microseconds.
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -45,6 +47,7 @@ __device__ __forceinline__ void load32(const int32_t* __restrict__ ids, int64_t 
 
 __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict__ ids, int64_t T,
                                                        int top_k, int E, int tile_rows,
+                                                       int small_rows,
                                                        int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ tile_base,
@@ -87,23 +90,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
             run += hist[i];
         }
         offs[E] = run;
-        if (e == 0) {
-            int tiles = 0;
-            for (int i = 0; i < E; ++i) {
-                tile_base[i] = tiles;
-                tiles += (hist[i] + tile_rows - 1) / tile_rows;
-            }
-            tile_base[E] = tiles;
-            tile_base[E + 1] = tiles + static_cast<int>((T + tile_rows - 1) / tile_rows);
-            int n = 0;  // decode chunks: the shared expert first, then routed experts
-            for (int64_t r = 0; r < T; r += kDecodeRows)
-                chunks[n++] = make_int4(E, static_cast<int>(P + r),
-                                        static_cast<int>(min(static_cast<int64_t>(kDecodeRows), T - r)), 0);
-            for (int i = 0; i < E; ++i)
-                for (int r = 0; r < hist[i]; r += kDecodeRows)
-                    chunks[n++] = make_int4(i, offs[i] + r, min(kDecodeRows, hist[i] - r), 0);
-            *nchunks = n;
-        }
+        if (e == 0) build_work_lists(hist, offs, E, T, P, tile_rows, small_rows, tile_base, chunks, nchunks);
     }
     __syncthreads();
     if (e == 0) {
@@ -143,10 +130,10 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
 }
 
 hipError_t launch_dispatch(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_rows,
-                           int32_t* counts, int32_t* offsets, int32_t* tile_base, int32_t* perm,
+                           int small_rows, int32_t* counts, int32_t* offsets, int32_t* tile_base, int32_t* perm,
                            int32_t* inv, int4* chunks, int32_t* nchunks, hipStream_t stream) {
     hipLaunchKernelGGL(dispatch_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, stream, ids,
-                       T, top_k, static_cast<int>(E), tile_rows, counts, offsets, tile_base, perm,
+                       T, top_k, static_cast<int>(E), tile_rows, small_rows, counts, offsets, tile_base, perm,
                        inv, chunks, nchunks);
     return hipGetLastError();
 }

@@ -49,14 +49,15 @@ hipError_t launch_topk(const float* partials, int slices, const float* bias, int
 // K2 + K3 for small batches in one block: logits, top-k, gates, counts, offsets,
 // GEMM tile table, perm, inv and the decode row chunks (int4: group, first row, rows, 0)
 hipError_t launch_route_small(const float* partials, int slices, const float* bias, int64_t T,
-                              int64_t E, int top_k, int tile_rows, float* logits, int32_t* ids,
+                              int64_t E, int top_k, int tile_rows, int small_rows, float* logits,
+                              int32_t* ids,
                               float* gates, int32_t* ids_copy, float* gates_copy, int32_t* counts,
                               int32_t* offsets, int32_t* tile_base, int32_t* perm, int32_t* inv,
                               int4* chunks, int32_t* nchunks, hipStream_t stream);
 
 // K3: counts, offsets, GEMM tile table, stable permutation and its inverse, decode chunks
 hipError_t launch_dispatch(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_rows,
-                           int32_t* counts, int32_t* offsets, int32_t* tile_base, int32_t* perm,
+                           int small_rows, int32_t* counts, int32_t* offsets, int32_t* tile_base, int32_t* perm,
                            int32_t* inv, int4* chunks, int32_t* nchunks, hipStream_t stream);
 
 struct GroupedGemmArgs {
@@ -111,8 +112,10 @@ struct DecodeArgs {
 };
 
 // K7: decode up / down projections over the row chunks
-hipError_t launch_decode_up(const DecodeArgs& a, int max_chunks, hipStream_t stream);
-hipError_t launch_decode_down(const DecodeArgs& a, int max_chunks, hipStream_t stream);
+hipError_t launch_decode_up(const DecodeArgs& a, int max_chunks, int shared_chunks,
+                            hipStream_t stream);
+hipError_t launch_decode_down(const DecodeArgs& a, int max_chunks, int shared_chunks,
+                              hipStream_t stream);
 
 // K6c: y[t] = O[P + t] + sum_j gate[t, j] * O[inv[t, j]]  -> bf16
 hipError_t launch_combine(const float* O, const float* gates, const int32_t* inv, int64_t T,

@@ -17,6 +17,7 @@
 // so the result does not depend on scheduling.
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -255,12 +256,12 @@ hipError_t launch_topk(const float* partials, int slices, const float* bias, int
 
 // ------------------------------------------------------------------------
 // Small-batch routing in one block: logits (slice sums + bias), top-k and
-// gates, then the dispatch (counts, offsets, stable perm / inv) and the list
-// of decode row chunks (<= 16 rows each; routed experts in id order, then the
-// shared expert). Used when T * E <= kSmallRouteLogits and T * top_k <= 1024.
+// gates, then the dispatch (counts, offsets, stable perm / inv) and the work
+// lists of the projections (build_work_lists). Used when T * E <= kSmallRouteLogits and T * top_k <= 1024.
 __global__ __launch_bounds__(256) void route_small_kernel(
     const float* __restrict__ partials, int slices, const float* __restrict__ bias, int64_t T,
-    int E, int top_k, int tile_rows, float* __restrict__ logits, int32_t* __restrict__ ids,
+    int E, int top_k, int tile_rows, int small_rows, float* __restrict__ logits,
+    int32_t* __restrict__ ids,
     float* __restrict__ gates, int32_t* __restrict__ ids_copy, float* __restrict__ gates_copy,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_base,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, int4* __restrict__ chunks,
@@ -313,23 +314,8 @@ __global__ __launch_bounds__(256) void route_small_kernel(
             perm[slot] = p;
             inv[p] = slot;
         }
-        int n = 0;  // shared expert first (the largest work items), then routed experts
-        for (int r = 0; r < T; r += kDecodeRows)
-            chunks[n++] = make_int4(E, P + r, static_cast<int>(T) - r < kDecodeRows ? static_cast<int>(T) - r
-                                                                             : kDecodeRows, 0);
-        for (int e = 0; e < E; ++e) {
-            const int c = off[e + 1] - off[e];
-            for (int r = 0; r < c; r += kDecodeRows)
-                chunks[n++] = make_int4(e, off[e] + r, c - r < kDecodeRows ? c - r : kDecodeRows, 0);
-        }
-        *nchunks = n;
-        int tiles = 0;
-        for (int e = 0; e < E; ++e) {
-            tile_base[e] = tiles;
-            tiles += (off[e + 1] - off[e] + tile_rows - 1) / tile_rows;
-        }
-        tile_base[E] = tiles;
-        tile_base[E + 1] = tiles + static_cast<int>((T + tile_rows - 1) / tile_rows);
+        // cnt[e] is back to expert e's pair count after the ranking loop
+        build_work_lists(cnt, off, E, T, P, tile_rows, small_rows, tile_base, chunks, nchunks);
     }
     __syncthreads();
     for (int e = tid; e < E; e += 256) {
@@ -340,12 +326,12 @@ __global__ __launch_bounds__(256) void route_small_kernel(
 }
 
 hipError_t launch_route_small(const float* partials, int slices, const float* bias, int64_t T,
-                              int64_t E, int top_k, int tile_rows, float* logits, int32_t* ids,
-                              float* gates, int32_t* ids_copy, float* gates_copy, int32_t* counts,
-                              int32_t* offsets, int32_t* tile_base, int32_t* perm, int32_t* inv,
-                              int4* chunks, int32_t* nchunks, hipStream_t stream) {
+                              int64_t E, int top_k, int tile_rows, int small_rows, float* logits,
+                              int32_t* ids, float* gates, int32_t* ids_copy, float* gates_copy,
+                              int32_t* counts, int32_t* offsets, int32_t* tile_base, int32_t* perm,
+                              int32_t* inv, int4* chunks, int32_t* nchunks, hipStream_t stream) {
     hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(256), 0, stream, partials, slices, bias, T,
-                       static_cast<int>(E), top_k, tile_rows, logits, ids, gates, ids_copy,
+                       static_cast<int>(E), top_k, tile_rows, small_rows, logits, ids, gates, ids_copy,
                        gates_copy, counts, offsets, tile_base, perm, inv, chunks, nchunks);
     return hipGetLastError();
 }

@@ -53,10 +53,13 @@ SMALL = {
     "tile edge 257": W.config(0).with_(T=257, E=2, d=384, top_k=1),
     "multi-block routing": W.config(0).with_(T=600, E=16, h=384, top_k=2),
     "k=16 of 40": W.config(0).with_(T=40, d=512, E=40, h=256, top_k=16),
+    # pairs per expert 283/189/66/31/15/8/3/1/1/2/1/0: GEMM tiles, two-chunk and
+    # one-chunk streamed experts and an empty one on the hybrid path
+    "mixed expert sizes": W.config(0).with_(T=300, E=12, top_k=2, bias="zipf", bias_param=0.6),
 }
 
 
-@pytest.mark.parametrize("path", ["prefill", "decode"])
+@pytest.mark.parametrize("path", ["prefill", "decode", "hybrid"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_layers_every_token(name, path):
     cfg = SMALL[name]
@@ -66,13 +69,14 @@ def test_small_layers_every_token(name, path):
     _check(layer, y, ids, np.arange(cfg.T))
 
 
-def test_tiny_layer_both_paths_agree():
+def test_tiny_layer_all_paths_agree():
     layer = build_layer(W.config(0))
     y1, i1, _ = _run(layer, "prefill")
-    y2, i2, _ = _run(layer, "decode")
-    np.testing.assert_array_equal(i1, i2)
-    err = row_errors(y1, y2.float().numpy().astype(np.float64))
-    assert err.max() <= 1e-2
+    for other in ("decode", "hybrid"):
+        y2, i2, _ = _run(layer, other)
+        np.testing.assert_array_equal(i1, i2)
+        err = row_errors(y1, y2.float().numpy().astype(np.float64))
+        assert err.max() <= 1e-2, other
 
 
 @pytest.mark.parametrize("i,nrows", [(1, 16), (2, 48), (3, 48), (4, 12)])
