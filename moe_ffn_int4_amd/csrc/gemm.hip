@@ -171,10 +171,12 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
     const int b_st = ASUB * SUB + (tid >> 4) * SUB;  // + frag_slot(tid & 15, q)
 
     constexpr int BV = ROUTED ? 1 : 4;
-    u32x4 ra[AP], rb[BV];
-    float rs = 0.f;
+    // two register sets: global data two steps ahead of the MFMAs
+    u32x4 ra0[AP], rb0[BV], ra1[AP], rb1[BV];
+    float rs0 = 0.f, rs1 = 0.f;
     // global -> registers for reduction step k
-    auto load_step = [&](int k) __attribute__((always_inline)) {
+    auto load_step = [&](u32x4 (&ra)[AP], u32x4 (&rb)[BV], float& rs, int k)
+                         __attribute__((always_inline)) {
         k = k < steps ? k : steps - 1;  // past the end: reload the last step (unused)
         const int64_t k0 = static_cast<int64_t>(k) * BK;
 #pragma unroll
@@ -191,7 +193,8 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         }
     };
     // registers -> LDS stage (int4 B dequantized on the way)
-    auto store_step = [&](int stage) __attribute__((always_inline)) {
+    auto store_step = [&](const u32x4 (&ra)[AP], const u32x4 (&rb)[BV], float rs, int stage)
+                          __attribute__((always_inline)) {
         uint8_t* st = lds + stage * STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < AP; ++i) *reinterpret_cast<u32x4*>(st + a_st + 4 * i * SUB) = ra[i];
@@ -236,23 +239,35 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
     };
 
-    load_step(0);
-    store_step(0);
+    // step k computes from LDS stage k & 1; its loop iteration first requests
+    // step k+2 into the register set it frees, then stores step k+1 (requested
+    // one step earlier) into the other stage after the MFMAs
+    load_step(ra0, rb0, rs0, 0);
+    load_step(ra1, rb1, rs1, 1);
+    store_step(ra0, rb0, rs0, 0);
     __syncthreads();
-    load_step(1);
+    load_step(ra0, rb0, rs0, 2);
     __builtin_amdgcn_sched_barrier(0);
     mfma_step(0, std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
-    store_step(1);
+    store_step(ra1, rb1, rs1, 1);
     __syncthreads();
-    for (int k = 1; k < steps; ++k) {
-        load_step(k + 1);
+    int k = 1;
+    for (; k + 1 < steps; k += 2) {
+        load_step(ra1, rb1, rs1, k + 2);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-        mfma_step(k & 1, std::false_type{});
+        mfma_step(1, std::false_type{});
         __builtin_amdgcn_sched_barrier(0);  // stores (which wait for the loads) after the MFMAs
-        store_step((k & 1) ^ 1);
+        store_step(ra0, rb0, rs0, 0);
+        __syncthreads();
+        load_step(ra0, rb0, rs0, k + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(0, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        store_step(ra1, rb1, rs1, 1);
         __syncthreads();
     }
+    mfma_step(1, std::false_type{});  // the last step (steps is even, so it is odd)
 
     // ---- epilogue: D[row][col], row = 4 * lq + r inside a 16 x 16 sub-tile, col = l16
     const int l16 = lane & 15, lq = lane >> 4;
