@@ -21,6 +21,10 @@ source set; no line numbers):
   ``(Swish(xW) * xV) W2`` with ``Swish(x) = x * sigmoid(x)``, from the
   docs.ifdog.com page "Llama 开源模型系列", section "SwiGLU：门控激活的数学".
   fp64 throughout (weights widened exactly).
+* ``moe.Bf16Expert`` -- routed experts held in bf16 instead of int4: the
+  pure-bf16 inference path, which the lshu.cn page lists (section
+  "三条推理路径差异") as the accuracy baseline of the quantized paths. The
+  forward is the same; the weights widen exactly.
 * ``native`` -- the same forward written as a plain C per-token loop
   (``csrc/oracle.c``), plus the quantizer as a plain C loop. It pins the
   grouped numpy form: both must agree.
@@ -34,6 +38,6 @@ against hand-worked groups, closed forms, invariants and brute force.
 """
 from .quantize import int4_group_quantize, dequantize  # noqa: F401
 from .moe import (  # noqa: F401
-    MoEResult, moe_forward, router_logits, select_topk, sigmoid, silu, swiglu,
-    shared_forward,
+    Bf16Expert, MoEResult, bf16_bits_to_f64, moe_forward, router_logits, select_topk, sigmoid,
+    silu, swiglu, shared_forward,
 )

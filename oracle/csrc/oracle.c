@@ -193,3 +193,37 @@ int oracle_moe_token(const double *x, int64_t d, int64_t h, int64_t E, int32_t k
     for (int64_t m = 0; m < d; ++m) y[m] += o[m];
     return 0;
 }
+
+/*
+ * oracle_moe_token with bf16 routed experts: the pure-bf16 path, which the
+ * lshu.cn page (section "三条推理路径差异") lists as the accuracy baseline.
+ * Expert e's weights are w1[e], w3[e], w2[e] (bf16 bits, widened exactly);
+ * everything else as in oracle_moe_token.
+ */
+int oracle_moe_token_bf16(const double *x, int64_t d, int64_t h, int64_t E, int32_t k,
+                          const float *wr, const float *bias,
+                          const uint16_t *const *w1, const uint16_t *const *w3,
+                          const uint16_t *const *w2,
+                          const uint16_t *sh1, const uint16_t *sh3, const uint16_t *sh2,
+                          const int32_t *forced_ids,
+                          float *logits, int32_t *ids, double *gates,
+                          double *u, double *o, double *y)
+{
+    oracle_router_token(x, wr, bias, E, d, logits);
+    if (forced_ids)
+        for (int32_t j = 0; j < k; ++j) ids[j] = forced_ids[j];
+    else
+        oracle_topk_token(logits, E, k, ids);
+
+    for (int64_t m = 0; m < d; ++m) y[m] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+        int32_t e = ids[j];
+        if (e < 0 || e >= E || !w1[e] || !w3[e] || !w2[e]) return -1;
+        gates[j] = sigmoid((double)logits[e]);
+        oracle_swiglu_bf16_token(x, d, h, w1[e], w3[e], w2[e], u, o);
+        for (int64_t m = 0; m < d; ++m) y[m] += gates[j] * o[m];
+    }
+    oracle_swiglu_bf16_token(x, d, h, sh1, sh3, sh2, u, o);
+    for (int64_t m = 0; m < d; ++m) y[m] += o[m];
+    return 0;
+}

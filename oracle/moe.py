@@ -78,6 +78,27 @@ class Int4Expert:
                 dequantize(self.c2, self.s2, group_size))
 
 
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) to fp64, exactly: a bf16 is the top half of an fp32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@dataclass
+class Bf16Expert:
+    """One routed expert held in bf16: the pure-bf16 inference path, which the
+    lshu.cn page (section "三条推理路径差异") lists as the accuracy baseline of the
+    int4 and fp8 paths. W1, W3 [h, d] and W2 [d, h] as bf16 bit patterns."""
+
+    w1: np.ndarray  # uint16 [h, d]
+    w3: np.ndarray  # uint16 [h, d]
+    w2: np.ndarray  # uint16 [d, h]
+
+    def dequantized(self, group_size: int = GROUP):
+        """The weights widened exactly to fp64 (group_size is unused)."""
+        return bf16_bits_to_f64(self.w1), bf16_bits_to_f64(self.w3), bf16_bits_to_f64(self.w2)
+
+
 @dataclass
 class MoEResult:
     y: np.ndarray        # [T, d] fp64 layer output
@@ -151,7 +172,8 @@ def shared_forward(x, s1, s3, s2) -> np.ndarray:
     return swiglu(x, s1, s3, s2)
 
 
-ExpertSource = Union[Sequence[Int4Expert], Callable[[int], Int4Expert]]
+ExpertSource = Union[Sequence[Union[Int4Expert, Bf16Expert]],
+                     Callable[[int], Union[Int4Expert, Bf16Expert]]]
 
 
 def moe_forward(x, wr, b, top_k: int, experts: ExpertSource, shared,
@@ -159,7 +181,8 @@ def moe_forward(x, wr, b, top_k: int, experts: ExpertSource, shared,
                 group_size: int = GROUP) -> MoEResult:
     """The MoE feed-forward layer on every row of ``x``.
 
-    ``experts`` is a sequence of ``Int4Expert`` or a callable ``e -> Int4Expert``
+    ``experts`` is a sequence of ``Int4Expert`` (or ``Bf16Expert``) or a callable
+    ``e -> expert``
     (so that large layers can be supplied one expert at a time; only experts
     that receive tokens are requested). ``shared`` is ``(S1, S3, S2)``.
     ``forced_ids`` [T, k], if given, replaces the top-k choice (the gates are

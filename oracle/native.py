@@ -13,7 +13,7 @@ from typing import Callable, Optional, Sequence, Union
 
 import numpy as np
 
-from .moe import Int4Expert, MoEResult, _f64
+from .moe import Bf16Expert, Int4Expert, MoEResult, _f64
 from .quantize import GROUP
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +58,9 @@ def lib():
         L.oracle_moe_token.argtypes = ([P, i64, i64, i64, i32, i64, P, P]
                                        + [P] * 6 + [P] * 3 + [P] + [P] * 6)
         L.oracle_moe_token.restype = ctypes.c_int
+        L.oracle_moe_token_bf16.argtypes = ([P, i64, i64, i64, i32, P, P]
+                                            + [P] * 3 + [P] * 3 + [P] + [P] * 6)
+        L.oracle_moe_token_bf16.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -89,7 +92,8 @@ def _bf16_bits(a) -> np.ndarray:
     return np.ascontiguousarray(a)
 
 
-ExpertSource = Union[Sequence[Optional[Int4Expert]], Callable[[int], Optional[Int4Expert]]]
+ExpertSource = Union[Sequence[Optional[Union[Int4Expert, Bf16Expert]]],
+                     Callable[[int], Optional[Union[Int4Expert, Bf16Expert]]]]
 
 
 def moe_forward_per_token(x, wr, b, top_k: int, experts: ExpertSource, shared,
@@ -122,10 +126,18 @@ def moe_forward_per_token(x, wr, b, top_k: int, experts: ExpertSource, shared,
                 a[e] = v.ctypes.data
         return a, keep
 
-    c1, k1 = arr("c1", np.int8); s1, k2 = arr("s1", np.float32)
-    c3, k3 = arr("c3", np.int8); s3, k4 = arr("s3", np.float32)
-    c2, k5 = arr("c2", np.int8); s2, k6 = arr("s2", np.float32)
-    keep = (k1, k2, k3, k4, k5, k6)  # noqa: F841  (keeps arrays alive)
+    bf16 = any(isinstance(ex, Bf16Expert) for ex in seq)
+    if bf16:
+        if not all(ex is None or isinstance(ex, Bf16Expert) for ex in seq):
+            raise TypeError("routed experts must be all int4 or all bf16")
+        w1, k1 = arr("w1", np.uint16); w3, k2 = arr("w3", np.uint16)
+        w2, k3 = arr("w2", np.uint16)
+        keep = (k1, k2, k3)  # noqa: F841  (keeps arrays alive)
+    else:
+        c1, k1 = arr("c1", np.int8); s1, k2 = arr("s1", np.float32)
+        c3, k3 = arr("c3", np.int8); s3, k4 = arr("s3", np.float32)
+        c2, k5 = arr("c2", np.int8); s2, k6 = arr("s2", np.float32)
+        keep = (k1, k2, k3, k4, k5, k6)  # noqa: F841  (keeps arrays alive)
 
     logits = np.empty((T, E), dtype=np.float32)
     ids = np.empty((T, top_k), dtype=np.int32)
@@ -136,12 +148,15 @@ def moe_forward_per_token(x, wr, b, top_k: int, experts: ExpertSource, shared,
     forced = None if forced_ids is None else np.ascontiguousarray(forced_ids, dtype=np.int32)
     L = lib()
     for t in range(T):
-        rc = L.oracle_moe_token(
-            _ptr(xf[t]), d, h, E, top_k, group_size, _ptr(wr),
-            None if bias is None else _ptr(bias),
-            c1, s1, c3, s3, c2, s2, _ptr(sh1), _ptr(sh3), _ptr(sh2),
-            None if forced is None else _ptr(forced[t]),
-            _ptr(logits[t]), _ptr(ids[t]), _ptr(gates[t]), _ptr(u), _ptr(o), _ptr(y[t]))
+        tail = (_ptr(sh1), _ptr(sh3), _ptr(sh2), None if forced is None else _ptr(forced[t]),
+                _ptr(logits[t]), _ptr(ids[t]), _ptr(gates[t]), _ptr(u), _ptr(o), _ptr(y[t]))
+        if bf16:
+            rc = L.oracle_moe_token_bf16(_ptr(xf[t]), d, h, E, top_k, _ptr(wr),
+                                         None if bias is None else _ptr(bias), w1, w3, w2, *tail)
+        else:
+            rc = L.oracle_moe_token(_ptr(xf[t]), d, h, E, top_k, group_size, _ptr(wr),
+                                    None if bias is None else _ptr(bias),
+                                    c1, s1, c3, s3, c2, s2, *tail)
         if rc != 0:
             raise ValueError(f"token {t}: a chosen expert's weights were not supplied")
     if top_k < E:
