@@ -47,7 +47,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", type=int, default=1, help="benchmark layer 0..4 (default 1)")
     ap.add_argument("--layers", type=int, default=None, help="independent layer copies to cycle")
-    ap.add_argument("--path", default="auto", choices=["auto", "prefill", "decode"])
+    ap.add_argument("--path", default="auto", choices=["auto", "prefill", "decode", "hybrid"])
+    ap.add_argument("--experts", default="int4", choices=["int4", "bf16"],
+                    help="routed expert weights: int4 g128 (default) or bf16 (the baseline path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -82,40 +84,53 @@ def measured_traffic(stage: str, workload: str):
     return rec["hbm_bytes_per_launch"]
 
 
-def layer_weight_bytes(cfg) -> int:
+def layer_weight_bytes(cfg, experts: str = "int4") -> int:
     g = 128
-    routed = cfg.E * 3 * (cfg.h * cfg.d // 2 + cfg.h * (cfg.d // g) * 4)
+    if experts == "bf16":
+        routed = cfg.E * 3 * cfg.h * cfg.d * 2
+    else:
+        routed = cfg.E * 3 * (cfg.h * cfg.d // 2 + cfg.h * (cfg.d // g) * 4)
     shared = 3 * cfg.h * cfg.d * 2
     return routed + shared
 
 
-def build_layer(cfg, dev):
+def build_layer(cfg, dev, experts: str = "int4"):
     import torch
     import moe_ffn_int4_amd as moe
     import workloads as W
     x = W.gen_x(cfg)
     wr, b = W.gen_router(cfg)
-    ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev)
+    if experts == "bf16":
+        ex = moe.Bf16Experts.empty(cfg.E, cfg.d, cfg.h, dev)
+    else:
+        ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev)
     for e in range(cfg.E):
         ws = [W.gen_expert_weight(cfg, w, e, dev) for w in ("w1", "w3", "w2")]
-        ex.quantize_expert(e, *ws)
+        if experts == "bf16":
+            ex.set_expert(e, *(w.to(torch.bfloat16) for w in ws))
+        else:
+            ex.quantize_expert(e, *ws)
         del ws
     shared_raw = W.gen_shared(cfg, dev)
     shared = moe.pack_shared(*shared_raw)
     torch.cuda.synchronize()
     return dict(cfg=cfg, x=x.to(dev), wr=wr.to(dev), b=None if b is None else b.to(dev),
-                experts=ex, shared=shared, shared_raw=shared_raw, x_cpu=x, wr_cpu=wr, b_cpu=b)
+                experts=ex, shared=shared, shared_raw=shared_raw, x_cpu=x, wr_cpu=wr, b_cpu=b,
+                routed=experts)
 
 
-def stage_units(cfg, counts):
+def stage_units(cfg, counts, experts: str = "int4"):
     """Algorithmic bytes and FLOPs of each stage for one launch, given the
     realized per-expert pair counts of the step."""
     g = 128
     T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.top_k
     P = T * k
     touched = int((counts > 0).sum())
-    w13 = 2 * (h * d // 2 + h * (d // g) * 4)   # one routed expert's W1 + W3 (int4 + scales)
-    w2 = d * h // 2 + d * (h // g) * 4          # its W2
+    if experts == "bf16":
+        w13, w2 = 2 * h * d * 2, d * h * 2          # one routed expert's W1 + W3, its W2
+    else:
+        w13 = 2 * (h * d // 2 + h * (d // g) * 4)   # one routed expert's W1 + W3 (int4 + scales)
+        w2 = d * h // 2 + d * (h // g) * 4          # its W2
     up_bytes = touched * w13 + 2 * h * d * 2 + T * d * 2 + (P + T) * h * 2
     down_bytes = touched * w2 + d * h * 2 + (P + T) * h * 2 + (P + T) * d * 4
     return {
@@ -137,7 +152,7 @@ def cpu_baseline(layer, n_sample, dev, min_seconds=10.0):
     import torch
     import workloads as W
     from oracle import native, router_logits, select_topk
-    from oracle.moe import Int4Expert
+    from oracle.moe import Bf16Expert, Int4Expert
 
     cfg = layer["cfg"]
     n = min(n_sample, cfg.T)
@@ -146,8 +161,13 @@ def cpu_baseline(layer, n_sample, dev, min_seconds=10.0):
     b = None if layer["b_cpu"] is None else layer["b_cpu"].numpy()
     ids, _ = select_topk(router_logits(xs, layer["wr_cpu"].numpy(), b), cfg.top_k)
     experts = [None] * cfg.E
-    for e in sorted(set(ids.ravel().tolist())):  # oracle's own quantization of the same draws
-        parts = []
+    for e in sorted(set(ids.ravel().tolist())):
+        if layer["routed"] == "bf16":  # the same bf16 rounding of the draws the GPU was given
+            experts[e] = Bf16Expert(*(
+                W.gen_expert_weight(cfg, w, e, dev).to(torch.bfloat16).cpu()
+                .view(torch.int16).numpy().view(np.uint16).copy() for w in ("w1", "w3", "w2")))
+            continue
+        parts = []  # oracle's own quantization of the same draws
         for w in ("w1", "w3", "w2"):
             parts.extend(native.quantize_int4(W.gen_expert_weight(cfg, w, e, dev).cpu().numpy()))
         experts[e] = Int4Expert(*parts)
@@ -198,12 +218,12 @@ def main() -> int:
     cfg0 = W.config(ci)
     steps = args.steps if args.steps is not None else DEFAULT_STEPS[ci]
     warmup = args.warmup if args.warmup is not None else DEFAULT_WARMUP[ci]
-    nlayers = args.layers or max(2, min(8, math.ceil(4e9 / layer_weight_bytes(cfg0))))
+    nlayers = args.layers or max(2, min(8, math.ceil(4e9 / layer_weight_bytes(cfg0, args.experts))))
     print(f"[bench] config {ci} {cfg0.name}: T={cfg0.T} d={cfg0.d} E={cfg0.E} h={cfg0.h} "
           f"k={cfg0.top_k}; {nlayers} layer copies, {warmup} warmup + {steps} timed steps",
           file=sys.stderr, flush=True)
 
-    layers = [build_layer(cfg0.with_(seed=s), dev) for s in range(nlayers)]
+    layers = [build_layer(cfg0.with_(seed=s), dev, args.experts) for s in range(nlayers)]
     ws = moe.alloc_workspace(cfg0.T, cfg0.d, cfg0.E, cfg0.h, cfg0.top_k, dev)
     y = torch.empty(cfg0.T, cfg0.d, dtype=torch.bfloat16, device=dev)
     ids = [torch.empty(cfg0.T, cfg0.top_k, dtype=torch.int32, device=dev) for _ in layers]
@@ -269,7 +289,7 @@ def main() -> int:
     value = cfg0.T * steps / wall
 
     # roofline of the dominant kernel, per launch, averaged over the timed steps
-    units = [stage_units(L["cfg"], c) for L, c in zip(layers, counts)]
+    units = [stage_units(L["cfg"], c, args.experts) for L, c in zip(layers, counts)]
     launched = {k: v for k, v in stages.items() if v[1] > 0}
     dom = max(launched, key=lambda k: launched[k][0])
     dom_ms, dom_n = launched[dom]
@@ -287,7 +307,7 @@ def main() -> int:
         achieved = flops / mean_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None}
-    roof["traffic"] = measured_traffic(dom, cfg0.name)
+    roof["traffic"] = measured_traffic(dom, cfg0.name if args.experts == "int4" else None)
     if roof["traffic"] is not None:
         roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
     roof["kernel"] = dom
@@ -321,7 +341,9 @@ def main() -> int:
         "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg0.name}: T={cfg0.T} d={cfg0.d} E={cfg0.E}+1 shared "
-                               f"h={cfg0.h} top_k={cfg0.top_k}, int4 g128 routed / bf16 shared",
+                               f"h={cfg0.h} top_k={cfg0.top_k}, "
+                               + ("int4 g128" if args.experts == "int4" else "bf16")
+                               + " routed / bf16 shared",
                    "T": cfg0.T, "d": cfg0.d, "E": cfg0.E, "h": cfg0.h, "top_k": cfg0.top_k,
                    "parallelism": "single GPU"},
         "roofline": roof,

@@ -174,6 +174,23 @@ int moe_forward_path(const moe_dims *dims, const uint16_t *x, const float *route
                      float *topk_gates, int32_t path, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/* Routed experts in bf16: the pure-bf16 inference path, which the lshu.cn
+ * page "Llama 4 单卡量化推理与选型指南" (section "三条推理路径差异") lists as
+ * the accuracy baseline of the int4 and fp8 paths. Each expert's matrix is
+ * packed by moe_pack_bf16_tiled and the experts are stacked:
+ *   w1, w3 [E] x tiled [h, d]: E*h*d bf16     w2 [E] x tiled [d, h]: E*d*h bf16 */
+typedef struct moe_experts_bf16 {
+    const uint16_t *w1, *w3, *w2;
+} moe_experts_bf16;
+
+/* moe_forward_path with bf16 routed experts: the same layer, workspace, paths,
+ * outputs and errors; the routed FFNs use the bf16 weights as given. */
+int moe_forward_bf16(const moe_dims *dims, const uint16_t *x, const float *router_w,
+                     const float *router_b, const moe_experts_bf16 *experts,
+                     const moe_shared_bf16 *shared, uint16_t *y, int32_t *topk_ids,
+                     float *topk_gates, int32_t path, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace moe_route alone needs (a prefix of the forward
  * workspace; 0 if dims are invalid; dims->h is ignored). */
 size_t moe_route_workspace_bytes(const moe_dims *dims);

@@ -53,6 +53,10 @@ class _Shared(ctypes.Structure):
     _fields_ = [("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
 
 
+class _ExpertsBf16(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -85,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.restype = ctypes.c_int
         L.moe_forward_path.argtypes = fwd + [i32, P, sz, P]
         L.moe_forward_path.restype = ctypes.c_int
+        fwd_bf16 = list(fwd)
+        fwd_bf16[4] = ctypes.POINTER(_ExpertsBf16)
+        L.moe_forward_bf16.argtypes = fwd_bf16 + [i32, P, sz, P]
+        L.moe_forward_bf16.restype = ctypes.c_int
         L.moe_route_workspace_bytes.argtypes = [ctypes.POINTER(_Dims)]
         L.moe_route_workspace_bytes.restype = sz
         L.moe_route.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P, P, sz, P]
@@ -240,12 +248,53 @@ def alloc_workspace(T: int, d: int, E: int, h: int, top_k: int, device) -> torch
     return torch.empty(workspace_bytes(T, d, E, h, top_k), dtype=torch.uint8, device=device)
 
 
+@dataclass
+class Bf16Experts:
+    """Stacked routed experts in bf16 (the pure-bf16 baseline path), each matrix in
+    the tiled order of ``pack_bf16_tiled``."""
+
+    w1: torch.Tensor  # bf16 [E, h, d]
+    w3: torch.Tensor  # bf16 [E, h, d]
+    w2: torch.Tensor  # bf16 [E, d, h]
+
+    @property
+    def E(self) -> int:
+        return self.w1.shape[0]
+
+    @property
+    def h(self) -> int:
+        return self.w1.shape[1]
+
+    @property
+    def d(self) -> int:
+        return self.w2.shape[1]
+
+    @staticmethod
+    def empty(E: int, d: int, h: int, device) -> "Bf16Experts":
+        b = torch.bfloat16
+        return Bf16Experts(torch.empty(E, h, d, dtype=b, device=device),
+                           torch.empty(E, h, d, dtype=b, device=device),
+                           torch.empty(E, d, h, dtype=b, device=device))
+
+    def set_expert(self, e: int, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor):
+        """Pack one expert's bf16 weights (W1, W3 [h, d], W2 [d, h]) into slot ``e``."""
+        pack_bf16_tiled(w1, self.w1[e])
+        pack_bf16_tiled(w3, self.w3[e])
+        pack_bf16_tiled(w2, self.w2[e])
+
+    def _struct(self) -> _ExpertsBf16:
+        for name in ("w1", "w3", "w2"):
+            _need(getattr(self, name), name, torch.bfloat16)
+        return _ExpertsBf16(self.w1.data_ptr(), self.w3.data_ptr(), self.w2.data_ptr())
+
+
 def forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor],
-            experts: Int4Experts, shared, top_k: int, path: str = "auto",
+            experts, shared, top_k: int, path: str = "auto",
             y: Optional[torch.Tensor] = None, topk_ids: Optional[torch.Tensor] = None,
             topk_gates: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The MoE layer: y bf16 [T, d]. ``shared`` = (S1 [h, d], S3 [h, d], S2 [d, h]) bf16."""
+    """The MoE layer: y bf16 [T, d]. ``experts``: ``Int4Experts`` or ``Bf16Experts``;
+    ``shared`` = (S1 [h, d], S3 [h, d], S2 [d, h]) bf16, packed by ``pack_shared``."""
     _need(x, "x", torch.bfloat16)
     T, d = x.shape
     E, h = router_w.shape[0], experts.h
@@ -270,7 +319,8 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Te
     dims = _dims(T, d, E, h, top_k)
     ex = experts._struct()
     sh = _Shared(s1.data_ptr(), s3.data_ptr(), s2.data_ptr())
-    _check(lib().moe_forward_path(
+    entry = lib().moe_forward_bf16 if isinstance(experts, Bf16Experts) else lib().moe_forward_path
+    _check(entry(
         ctypes.byref(dims), _ptr(x), _ptr(router_w), _ptr(router_b), ctypes.byref(ex),
         ctypes.byref(sh), _ptr(y), _ptr(topk_ids), _ptr(topk_gates), PATHS[path],
         _ptr(workspace), workspace.numel(), _stream(x.device)))

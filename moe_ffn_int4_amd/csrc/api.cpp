@@ -402,20 +402,28 @@ int moe_route(const moe_dims* dims, const uint16_t* x, const float* router_w,
     return MOE_OK;
 }
 
-int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* router_w,
-                     const float* router_b, const moe_experts_int4* ex, const moe_shared_bf16* sh,
-                     uint16_t* y, int32_t* topk_ids, float* topk_gates, int32_t path,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+// The forward for int4 (ex4) or bf16 (exb) routed experts; exactly one is set.
+static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* router_w,
+                        const float* router_b, const moe_experts_int4* ex4,
+                        const moe_experts_bf16* exb, const moe_shared_bf16* sh, uint16_t* y,
+                        int32_t* topk_ids, float* topk_gates, int32_t path, void* workspace,
+                        size_t workspace_bytes, void* stream) {
     g_last_error.clear();
     CHECK(check_forward_args(dims, x, router_w, router_b, workspace, workspace_bytes));
-    if (!ex) return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
+    if (!ex4 && !exb) return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
     if (!sh) return fail(MOE_ERR_INVALID_ARG, "shared is NULL");
-    CHECK(check_ptr(ex->w1q, "experts->w1q"));
-    CHECK(check_ptr(ex->w3q, "experts->w3q"));
-    CHECK(check_ptr(ex->w2q, "experts->w2q"));
-    CHECK(check_ptr(ex->w1s, "experts->w1s", 4));
-    CHECK(check_ptr(ex->w3s, "experts->w3s", 4));
-    CHECK(check_ptr(ex->w2s, "experts->w2s", 4));
+    if (ex4) {
+        CHECK(check_ptr(ex4->w1q, "experts->w1q"));
+        CHECK(check_ptr(ex4->w3q, "experts->w3q"));
+        CHECK(check_ptr(ex4->w2q, "experts->w2q"));
+        CHECK(check_ptr(ex4->w1s, "experts->w1s", 4));
+        CHECK(check_ptr(ex4->w3s, "experts->w3s", 4));
+        CHECK(check_ptr(ex4->w2s, "experts->w2s", 4));
+    } else {
+        CHECK(check_ptr(exb->w1, "experts->w1"));
+        CHECK(check_ptr(exb->w3, "experts->w3"));
+        CHECK(check_ptr(exb->w2, "experts->w2"));
+    }
     CHECK(check_ptr(sh->s1, "shared->s1"));
     CHECK(check_ptr(sh->s3, "shared->s3"));
     CHECK(check_ptr(sh->s2, "shared->s2"));
@@ -442,8 +450,9 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
                                     (path == MOE_PATH_AUTO && P < kHybridAvgPairs * d.E));
     const int small_rows = decode ? -1 : (hybrid ? kHybridRows : 0);
     uint16_t* x_perm = reinterpret_cast<uint16_t*>(base + L.x_perm);
+    // the interleaved copy of x feeds only the streaming kernel's int4 experts
     CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates,
-                      decode || hybrid ? x_perm : nullptr, small_rows, s));
+                      (decode || hybrid) && ex4 ? x_perm : nullptr, small_rows, s));
 
     // streaming projections over the chunk list: every group (decode path) or
     // the small routed experts (hybrid path)
@@ -460,10 +469,15 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
         a.a_perm = x_perm;
         a.K = d.d;
         a.N = d.h;
-        a.wq0 = ex->w1q;
-        a.ws0 = ex->w1s;
-        a.wq1 = ex->w3q;
-        a.ws1 = ex->w3s;
+        if (ex4) {
+            a.wq0 = ex4->w1q;
+            a.ws0 = ex4->w1s;
+            a.wq1 = ex4->w3q;
+            a.ws1 = ex4->w3s;
+        } else {
+            a.wb0 = exb->w1;
+            a.wb1 = exb->w3;
+        }
         a.sh0 = sh->s1;
         a.sh1 = sh->s3;
         a.h_out = H;
@@ -483,8 +497,12 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
         a.a_perm = H;  // routed rows of H were written interleaved by the streaming up projection
         a.K = d.h;
         a.N = d.d;
-        a.wq0 = ex->w2q;
-        a.ws0 = ex->w2s;
+        if (ex4) {
+            a.wq0 = ex4->w2q;
+            a.ws0 = ex4->w2s;
+        } else {
+            a.wb0 = exb->w2;
+        }
         a.sh0 = sh->s2;
         a.o_out = O;
         return timed(MOE_STAGE_DECODE_DOWN, s, "decode down launch",
@@ -495,9 +513,12 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
         (d.E < P ? d.E : P) * ((kHybridRows + moe::kDecodeRows - 1) / moe::kDecodeRows);
 
     if (decode) {
-        const int shared_chunks = static_cast<int>((d.T + moe::kDecodeRows - 1) / moe::kDecodeRows);
-        CHECK(stream_up(L.max_chunks, shared_chunks));
-        CHECK(stream_down(L.max_chunks, shared_chunks));
+        // bf16 chunks are split four ways: the shared expert's, at the head of
+        // the list, or every chunk when the routed experts are bf16
+        const int split = ex4 ? static_cast<int>((d.T + moe::kDecodeRows - 1) / moe::kDecodeRows)
+                              : L.max_chunks;
+        CHECK(stream_up(L.max_chunks, split));
+        CHECK(stream_down(L.max_chunks, split));
     } else {
         moe::GroupedGemmArgs g{};
         g.T = d.T;
@@ -512,36 +533,70 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
         g.a = x;
         g.K = d.d;
         g.N = d.h;
-        g.wq0 = ex->w1q;
-        g.ws0 = ex->w1s;
-        g.wq1 = ex->w3q;
-        g.ws1 = ex->w3s;
+        if (ex4) {
+            g.wq0 = ex4->w1q;
+            g.ws0 = ex4->w1s;
+            g.wq1 = ex4->w3q;
+            g.ws1 = ex4->w3s;
+        } else {
+            g.wb0 = exb->w1;
+            g.wb1 = exb->w3;
+        }
         g.sh0 = sh->s1;
         g.sh1 = sh->s3;
         g.h_out = H;
         CHECK(timed(MOE_STAGE_UP, s, "grouped up launch", [&] { return moe::launch_grouped_up(g, s); }));
-        if (hybrid) CHECK(stream_up(static_cast<int>(hybrid_chunks), 0));
+        const int hsplit = ex4 ? 0 : static_cast<int>(hybrid_chunks);
+        if (hybrid) CHECK(stream_up(static_cast<int>(hybrid_chunks), hsplit));
 
         g.a = H;
         g.K = d.h;
         g.N = d.d;
-        g.wq0 = ex->w2q;
-        g.ws0 = ex->w2s;
+        g.wq0 = ex4 ? ex4->w2q : nullptr;
+        g.ws0 = ex4 ? ex4->w2s : nullptr;
         g.wq1 = nullptr;
         g.ws1 = nullptr;
+        g.wb0 = ex4 ? nullptr : exb->w2;
+        g.wb1 = nullptr;
         g.sh0 = sh->s2;
         g.sh1 = nullptr;
         g.h_out = nullptr;
         g.o_out = O;
         CHECK(timed(MOE_STAGE_DOWN, s, "grouped down launch",
                     [&] { return moe::launch_grouped_down(g, s); }));
-        if (hybrid) CHECK(stream_down(static_cast<int>(hybrid_chunks), 0));
+        if (hybrid) CHECK(stream_down(static_cast<int>(hybrid_chunks), hsplit));
     }
 
     CHECK(timed(MOE_STAGE_COMBINE, s, "combine launch", [&] {
         return moe::launch_combine(O, R.gates, R.inv, d.T, P, d.top_k, d.d, y, s);
     }));
     return MOE_OK;
+}
+
+int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* router_w,
+                     const float* router_b, const moe_experts_int4* experts,
+                     const moe_shared_bf16* shared, uint16_t* y, int32_t* topk_ids,
+                     float* topk_gates, int32_t path, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    if (!experts) {
+        g_last_error.clear();
+        return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
+    }
+    return forward_impl(dims, x, router_w, router_b, experts, nullptr, shared, y, topk_ids,
+                        topk_gates, path, workspace, workspace_bytes, stream);
+}
+
+int moe_forward_bf16(const moe_dims* dims, const uint16_t* x, const float* router_w,
+                     const float* router_b, const moe_experts_bf16* experts,
+                     const moe_shared_bf16* shared, uint16_t* y, int32_t* topk_ids,
+                     float* topk_gates, int32_t path, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    if (!experts) {
+        g_last_error.clear();
+        return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
+    }
+    return forward_impl(dims, x, router_w, router_b, nullptr, experts, shared, y, topk_ids,
+                        topk_gates, path, workspace, workspace_bytes, stream);
 }
 
 int moe_forward(const moe_dims* dims, const uint16_t* x, const float* router_w,

@@ -177,12 +177,13 @@ template <bool UP, int DR, int DS, int DL>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     // routed chunks of at most a.lds_rows rows keep their A rows in LDS
     extern __shared__ __attribute__((aligned(16))) uint16_t a_lds[];
-    // Rows 0 .. max_chunks-1 of the grid take the chunks; the shared expert's
-    // chunks (listed first) get three more rows each (max_chunks + 3 c + s - 1):
-    // shared sub-block s = 0..3 of a 64-feature range covers its 16 features
+    // Rows 0 .. max_chunks-1 of the grid take the chunks; chunks of bf16 weights
+    // at the head of the list (the shared expert's, or all of them when the
+    // routed experts are bf16) get three more rows each (max_chunks + 3 c + s - 1):
+    // sub-block s = 0..3 of a 64-feature range covers its 16 features
     // s*16 .. s*16+15 with all four waves, each wave a quarter of the reduction.
-    // Shared chunks stream bf16 weights (4x the bytes of an int4 chunk); split
-    // this way they spread over four times as many blocks and CUs.
+    // bf16 chunks stream 4x the bytes of an int4 chunk; split this way they
+    // spread over four times as many blocks and CUs.
     int c = blockIdx.y, sub = 0;
     if (c >= a.max_chunks) {
         const int e = c - a.max_chunks;
@@ -193,15 +194,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const int4 ch = a.chunks[c];
     const int group = ch.x, row0 = ch.y, nrows = ch.z;
     const bool routed = group < a.E;
-    if (routed && blockIdx.y >= a.max_chunks) return;
+    const bool int4 = routed && !a.wb0;  // otherwise bf16 weights (shared, or bf16 routed)
+    if (int4 && blockIdx.y >= a.max_chunks) return;
     const int64_t K = a.K, N = a.N;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kq = lane >> 4;
-    const int64_t n = static_cast<int64_t>(blockIdx.x) * 64 + (routed ? wave : sub) * 16 + l16;  // B column
+    const int64_t n = static_cast<int64_t>(blockIdx.x) * 64 + (int4 ? wave : sub) * 16 + l16;  // B column
     const int ng = static_cast<int>(K / kGroup);
 
-    // A row of MFMA row l16: routed experts read the interleaved copy, the shared
-    // expert the natural one. Rows past the chunk repeat its last row: their
+    // A row of MFMA row l16: int4 routed experts read the interleaved copy, bf16
+    // weights the natural one. Rows past the chunk repeat its last row: their
     // outputs are never stored, and every lane then loads unconditionally, which
     // keeps the load counter of the prefetch ring exact. Step i of group g uses
     // columns 128g + 32kq + 8i.. (int4: this lane's 32 codes) or 128g + 32i + 8kq..
@@ -210,10 +212,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     int64_t src;
     if (UP) src = routed ? a.perm[row0 + m] / a.top_k : row0 + m - a.P;
     else src = row0 + m;
-    const uint16_t* arow = (routed ? a.a_perm : a.a) + src * K + (routed ? kq * 32 : kq * 8);
+    const uint16_t* arow = (int4 ? a.a_perm : a.a) + src * K + (int4 ? kq * 32 : kq * 8);
 
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    if (routed && nrows <= a.lds_rows) {
+    if (int4 && nrows <= a.lds_rows) {
         // Stage the chunk's A rows (interleaved copies) in LDS once; the weight
         // ring then carries only weights and scales, and A comes from LDS.
         constexpr int D = DL;
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < D; ++u)
             if (u < ng - full) compute_lds<UP>(sl[u], lrow, full + u, acc0, acc1);
-    } else if (routed) {
+    } else if (int4) {
         constexpr int D = DR;
         constexpr int U = D + 1;
         // tile row block of this lane's feature; tiles of a row block are consecutive
@@ -282,8 +284,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         const int cnt = ((wave + 1) * ng) / 4 - gb;
         const int last = cnt > 0 ? cnt - 1 : 0;
         const int64_t rb = n >> 4;
-        const uint16_t* h0 = a.sh0 + rb * ng * 2048 + l16 * 32 + kq * 8 + gb * 2048;
-        const uint16_t* h1 = UP ? a.sh1 + rb * ng * 2048 + l16 * 32 + kq * 8 + gb * 2048 : nullptr;
+        const int64_t mat = routed ? static_cast<int64_t>(group) * N * K : 0;  // expert's matrix
+        const uint16_t* w0 = routed ? a.wb0 + mat : a.sh0;
+        const uint16_t* w1 = routed ? (UP ? a.wb1 + mat : nullptr) : a.sh1;
+        const uint16_t* h0 = w0 + rb * ng * 2048 + l16 * 32 + kq * 8 + gb * 2048;
+        const uint16_t* h1 = UP ? w1 + rb * ng * 2048 + l16 * 32 + kq * 8 + gb * 2048 : nullptr;
         const uint16_t* ar = arow + gb * kGroup;
         SharedSlot sl[U];
 #pragma unroll
@@ -324,7 +329,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 
     // D[m][n]: m = 4 * kq + r (token row of the chunk), n = l16 (this lane's feature)
     // up: routed rows of H are stored with 8-blocks interleaved for the down projection
-    const int64_t hcol = routed ? ((n & ~7LL) | (((n & 3) << 1) | ((n >> 2) & 1))) : n;
+    const int64_t hcol = int4 ? ((n & ~7LL) | (((n & 3) << 1) | ((n >> 2) & 1))) : n;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int mr = kq * 4 + r;

@@ -123,6 +123,9 @@ __device__ __forceinline__ int frag_slot(int n, int q) {
 template <bool UP, bool ROUTED>
 __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& tile, int nt,
                                           uint8_t* lds) {
+    // ROUTED: int4 B (routed experts); otherwise bf16 B: the shared expert, or
+    // routed experts held in bf16 (wb0 / wb1)
+    const bool routed_rows = tile.group < a.E;
     constexpr int SUB = 1024;                 // bytes per 16 x 32 sub-tile
     constexpr int ASUB = BM / 16;             // 8 A sub-tiles
     constexpr int STAGE_BYTES = (ASUB + 16) * SUB;  // 8 A + 16 B sub-tiles
@@ -143,7 +146,7 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         r = r < tile.nrows ? r : tile.nrows - 1;
         const int64_t s = tile.row0 + r;
         int64_t src;
-        if (UP) src = ROUTED ? a.perm[s] / a.top_k : s - a.P;
+        if (UP) src = routed_rows ? a.perm[s] / a.top_k : s - a.P;
         else src = s;
         arow[i] = a.a + src * K + (tid & 3) * 8;
     }
@@ -165,7 +168,11 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         bq = q + rb * ng * 1024 + (bn & 15) * 64;  // + group * 1024 + quarter * 16
         bs = sc + rb * ng * 16 + (bn & 15);          // + group * 16
     } else {
-        const uint16_t* src = (UP && tid >= 128) ? a.sh1 : a.sh0;
+        const uint16_t* src;
+        if (routed_rows)
+            src = ((UP && tid >= 128) ? a.wb1 : a.wb0) + static_cast<int64_t>(tile.group) * N * K;
+        else
+            src = (UP && tid >= 128) ? a.sh1 : a.sh0;
         bh = src + (bn >> 4) * ng * 2048 + (bn & 15) * 32;  // + group*2048 + quarter*512 + 8q
     }
     const int b_st = ASUB * SUB + (tid >> 4) * SUB;  // + frag_slot(tid & 15, q)
@@ -318,7 +325,7 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(GroupedGemmArgs a) 
 
     Tile tile;
     if (!find_tile(a, mt, tile)) return;
-    if (tile.group < a.E) gemm_tile<UP, true>(a, tile, nt, lds);
+    if (tile.group < a.E && !a.wb0) gemm_tile<UP, true>(a, tile, nt, lds);
     else gemm_tile<UP, false>(a, tile, nt, lds);
 }
 

@@ -78,6 +78,8 @@ struct GroupedGemmArgs {
     const float* ws1;
     const uint16_t* sh0;     // up: S1, down: S2 (bf16 [N, K])
     const uint16_t* sh1;     // up: S3
+    const uint16_t* wb0;     // bf16 routed experts instead of int4 (null: int4):
+    const uint16_t* wb1;     //   up: W1 / W3, down: W2 (tiled bf16 [E, N, K])
     uint16_t* h_out;         // up: H [P + T, h] bf16
     float* o_out;            // down: O [P + T, d] fp32
 };
@@ -105,6 +107,8 @@ struct DecodeArgs {
     const float* ws1;
     const uint16_t* sh0;
     const uint16_t* sh1;
+    const uint16_t* wb0;     // bf16 routed experts instead of int4 (null: int4)
+    const uint16_t* wb1;
     uint16_t* h_out;
     float* o_out;
     int lds_rows;            // set by the launcher: routed chunks this small stage A in LDS

@@ -16,7 +16,7 @@ import torch
 import moe_ffn_int4_amd as moe
 import workloads as W
 from oracle import native
-from oracle.moe import Int4Expert
+from oracle.moe import Bf16Expert, Int4Expert
 
 TOL = 2e-2  # max relative error of an output row (infinity norm)
 MARGIN = 1e-4  # top-k margin above which expert ids must match exactly
@@ -40,32 +40,49 @@ class Layer:
     wr_d: torch.Tensor
     b_d: Optional[torch.Tensor]
     shared_d: tuple
-    experts_d: moe.Int4Experts
+    experts_d: object        # moe.Int4Experts or moe.Bf16Experts
+    routed: str = "int4"     # routed expert weights: "int4" or "bf16"
 
 
-def build_layer(cfg: W.MoEConfig, dev="cuda:0", routed_draw: Optional[str] = None) -> Layer:
+def build_layer(cfg: W.MoEConfig, dev="cuda:0", routed_draw: Optional[str] = None,
+                routed: str = "int4") -> Layer:
     """The layer on the GPU. Routed weights are drawn on the CPU for small
-    layers and on the GPU (then quantized there) for the 5120 x 8192 ones."""
+    layers and on the GPU (then quantized there) for the 5120 x 8192 ones.
+    ``routed="bf16"`` keeps the routed experts in bf16 (RNE of the same draws)."""
     dev = torch.device(dev)
     if routed_draw is None:
         routed_draw = "cpu" if cfg.d * cfg.h <= 1 << 22 else str(dev)
     x = W.gen_x(cfg)
     wr, b = W.gen_router(cfg)
     shared = W.gen_shared(cfg)
-    ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev)
+    if routed == "bf16":
+        ex = moe.Bf16Experts.empty(cfg.E, cfg.d, cfg.h, dev)
+    else:
+        ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev)
     for e in range(cfg.E):
         ws = [W.gen_expert_weight(cfg, w, e, routed_draw).to(dev) for w in ("w1", "w3", "w2")]
-        ex.quantize_expert(e, *ws)
+        if routed == "bf16":
+            ex.set_expert(e, *(w.to(torch.bfloat16) for w in ws))
+        else:
+            ex.quantize_expert(e, *ws)
         del ws
     torch.cuda.synchronize(dev)
     shared_d = moe.pack_shared(*(s.to(dev) for s in shared))
     torch.cuda.synchronize(dev)
     return Layer(cfg, x, wr, b, shared, routed_draw, dev, x.to(dev), wr.to(dev),
-                 None if b is None else b.to(dev), shared_d, ex)
+                 None if b is None else b.to(dev), shared_d, ex, routed)
 
 
-def oracle_expert(layer: Layer, e: int) -> Int4Expert:
-    """Expert e quantized by the oracle from the same fp32 draw."""
+def oracle_expert(layer: Layer, e: int):
+    """Expert e for the oracle from the same fp32 draw: quantized by the oracle
+    (int4 layers), or the same bf16 rounding the GPU was given (bf16 layers)."""
+    if layer.routed == "bf16":
+        bits = []
+        for w in ("w1", "w3", "w2"):
+            wb = W.gen_expert_weight(layer.cfg, w, e, layer.gen_dev).to(torch.bfloat16).cpu()
+            bits.append(wb.view(torch.int16).numpy().view(np.uint16).copy())
+            del wb
+        return Bf16Expert(*bits)
     parts = []
     for w in ("w1", "w3", "w2"):
         wf = W.gen_expert_weight(layer.cfg, w, e, layer.gen_dev).cpu().numpy()
@@ -94,7 +111,7 @@ def oracle_forward_rows(layer: Layer, rows: np.ndarray, gpu_ids: Optional[np.nda
             forced[tie] = gpu_ids[rows][tie]
             ids = forced
     need = sorted(set(int(e) for e in np.unique(ids)))
-    experts: List[Optional[Int4Expert]] = [None] * cfg.E
+    experts: List = [None] * cfg.E
     for e in need:
         experts[e] = oracle_expert(layer, e)
     r = native.moe_forward_per_token(xs, layer.wr.numpy(), b, cfg.top_k, experts, layer.shared,
