@@ -203,8 +203,12 @@ def moe_forward(x, wr, b, top_k: int, experts: ExpertSource, shared,
         t_idx, j_idx = np.nonzero(ids == e)  # pairs routed to e, in (t, j) order
         if t_idx.size == 0:
             continue
-        w1, w3, w2 = get(e).dequantized(group_size)
-        out = swiglu(xf[t_idx], w1, w3, w2)
+        ex = get(e)
+        if hasattr(ex, "ffn"):  # experts with their own arithmetic (fp8 row-wise)
+            out = ex.ffn(xf[t_idx])
+        else:
+            w1, w3, w2 = ex.dequantized(group_size)
+            out = swiglu(xf[t_idx], w1, w3, w2)
         scatter_add(y, t_idx, gates[t_idx, j_idx], out)
     y += shared_forward(xf, *shared)
     return MoEResult(y=y, ids=ids, gates=gates, logits=logits, margin=margin)
