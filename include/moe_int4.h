@@ -174,6 +174,27 @@ int moe_forward_path(const moe_dims *dims, const uint16_t *x, const float *route
                      float *topk_gates, int32_t path, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/* Row-wise fp8 (OCP E4M3) quantization of the fp8 routed-expert path: the
+ * lshu.cn page (section "量化环节") quantizes each activation row to fp8 with
+ * its scale bounded by activation_scale_ub, and holds the weights in fp8 with
+ * one scale per row ("FP8 行级", section "三条推理路径差异"). Per row of K
+ * values, in fp32 with a correctly rounded division:
+ *   scale = min(max(max|v|, 1e-12), ub) / 448,   code = fp8_rne(clamp(v / scale, -448, 448))
+ * (no bound for weights; ub <= 0: no bound).
+ *
+ * moe_quantize_fp8_tiled: weights, w fp32 [rows, K] row-major, rows % 16 == 0,
+ *   K % 128 == 0 -> q [rows * K] bytes in the tiled order the forward reads
+ *   (tile t = (row/16)*(K/128) + k/128 of 2 KB; byte
+ *   t*2048 + ((k%128)/32)*512 + (row%16)*32 + k%32), scales fp32 [rows].
+ *   w 16-byte aligned; q and scales 4-byte aligned.
+ * moe_quantize_fp8_rows: activations, x bf16 [rows, K] row-major -> q [rows, K]
+ *   row-major codes, scales fp32 [rows]. x 8-byte aligned.
+ * Both: INVALID_ARG on bad shapes / pointers; asynchronous on `stream`. */
+int moe_quantize_fp8_tiled(const float *w, int64_t rows, int64_t K, uint8_t *q, float *scales,
+                           void *stream);
+int moe_quantize_fp8_rows(const uint16_t *x, int64_t rows, int64_t K, float ub, uint8_t *q,
+                          float *scales, void *stream);
+
 /* Routed experts in bf16: the pure-bf16 inference path, which the lshu.cn
  * page "Llama 4 单卡量化推理与选型指南" (section "三条推理路径差异") lists as
  * the accuracy baseline of the int4 and fp8 paths. Each expert's matrix is

@@ -92,6 +92,10 @@ def lib() -> ctypes.CDLL:
         fwd_bf16 = list(fwd)
         fwd_bf16[4] = ctypes.POINTER(_ExpertsBf16)
         L.moe_forward_bf16.argtypes = fwd_bf16 + [i32, P, sz, P]
+        L.moe_quantize_fp8_tiled.argtypes = [P, i64, i64, P, P, P]
+        L.moe_quantize_fp8_tiled.restype = ctypes.c_int
+        L.moe_quantize_fp8_rows.argtypes = [P, i64, i64, ctypes.c_float, P, P, P]
+        L.moe_quantize_fp8_rows.restype = ctypes.c_int
         L.moe_forward_bf16.restype = ctypes.c_int
         L.moe_route_workspace_bytes.argtypes = [ctypes.POINTER(_Dims)]
         L.moe_route_workspace_bytes.restype = sz
@@ -178,6 +182,39 @@ def pack_bf16_tiled(src: torch.Tensor, dst: Optional[torch.Tensor] = None) -> to
     _need(dst, "dst", torch.bfloat16, (rows, K))
     _check(lib().moe_pack_bf16_tiled(_ptr(src), rows, K, _ptr(dst), _stream(src.device)))
     return dst
+
+
+def quantize_fp8(w: torch.Tensor, q: Optional[torch.Tensor] = None,
+                 scales: Optional[torch.Tensor] = None):
+    """fp32 weights [rows, K] -> fp8 E4M3 codes (uint8, tiled order) and fp32 row scales."""
+    _need(w, "w", torch.float32)
+    rows, K = w.shape
+    if q is None:
+        q = torch.empty(rows, K, dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=w.device)
+    _need(q, "q", torch.uint8, (rows, K))
+    _need(scales, "scales", torch.float32, (rows,))
+    _check(lib().moe_quantize_fp8_tiled(_ptr(w), rows, K, _ptr(q), _ptr(scales), _stream(w.device)))
+    return q, scales
+
+
+def quantize_fp8_rows(x: torch.Tensor, ub: float):
+    """bf16 activations [rows, K] -> row-major fp8 codes and fp32 row scales
+    (the row maximum bounded by ``ub``; ``ub <= 0``: no bound)."""
+    _need(x, "x", torch.bfloat16)
+    rows, K = x.shape
+    q = torch.empty(rows, K, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(lib().moe_quantize_fp8_rows(_ptr(x), rows, K, float(ub), _ptr(q), _ptr(scales),
+                                       _stream(x.device)))
+    return q, scales
+
+
+def untile_fp8(q: torch.Tensor, rows: int, K: int) -> torch.Tensor:
+    """Tiled fp8 codes back to row-major [rows, K] (CPU or GPU tensor)."""
+    t = q.reshape(rows // 16, K // 128, 4, 16, 32)  # row tile, k tile, step, row, column
+    return t.permute(0, 3, 1, 2, 4).reshape(rows, K)
 
 
 def pack_shared(s1: torch.Tensor, s3: torch.Tensor, s2: torch.Tensor):

@@ -361,6 +361,42 @@ int moe_pack_bf16_tiled(const uint16_t* src, int64_t rows, int64_t K, uint16_t* 
     return MOE_OK;
 }
 
+int moe_quantize_fp8_tiled(const float* w, int64_t rows, int64_t K, uint8_t* q, float* scales,
+                           void* stream) {
+    g_last_error.clear();
+    if (rows < 0 || rows % 16)
+        return fail(MOE_ERR_INVALID_ARG, "rows = %lld must be a non-negative multiple of 16",
+                    (long long)rows);
+    if (K < 128 || K % 128)
+        return fail(MOE_ERR_INVALID_ARG, "K = %lld must be a positive multiple of 128", (long long)K);
+    if (rows == 0) return MOE_OK;
+    CHECK(check_ptr(w, "w"));
+    CHECK(check_ptr(q, "q", 4));
+    CHECK(check_ptr(scales, "scales", 4));
+    CHECK(device_ok());
+    HIP_CHECK(moe::launch_quantize_fp8_weights(w, rows, K, q, scales, static_cast<hipStream_t>(stream)),
+              "fp8 quantize launch");
+    return MOE_OK;
+}
+
+int moe_quantize_fp8_rows(const uint16_t* x, int64_t rows, int64_t K, float ub, uint8_t* q,
+                          float* scales, void* stream) {
+    g_last_error.clear();
+    if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows = %lld is negative", (long long)rows);
+    if (K < 128 || K % 128)
+        return fail(MOE_ERR_INVALID_ARG, "K = %lld must be a positive multiple of 128", (long long)K);
+    if (!(ub >= 0.f) || ub > 3.0e38f) return fail(MOE_ERR_INVALID_ARG, "ub must be finite and >= 0");
+    if (rows == 0) return MOE_OK;
+    CHECK(check_ptr(x, "x", 8));
+    CHECK(check_ptr(q, "q", 4));
+    CHECK(check_ptr(scales, "scales", 4));
+    CHECK(device_ok());
+    HIP_CHECK(moe::launch_quantize_fp8_activations(x, rows, K, ub, q, scales,
+                                                   static_cast<hipStream_t>(stream)),
+              "fp8 activation quantize launch");
+    return MOE_OK;
+}
+
 size_t moe_forward_workspace_bytes(const moe_dims* dims) {
     const std::string saved = g_last_error;
     if (check_dims(dims) != MOE_OK) return 0;

@@ -26,6 +26,14 @@ constexpr int kSmallRoutePairs = 1024;
 // K1 (row-major groups, or the 16-row tiles the forward pass reads)
 hipError_t launch_quantize_int4(const float* w, int64_t rows, int64_t K, uint8_t* q,
                                 float* scales, bool tiled, hipStream_t stream);
+// fp8 (E4M3) row-wise quantization: weights fp32 [rows, K] -> tiled codes
+// (16 x 128 tiles of 4 steps x 16 rows x 32 bytes) + per-row scales;
+// activations bf16 [rows, K] -> row-major codes + per-row scales (ub > 0
+// bounds a row's maximum)
+hipError_t launch_quantize_fp8_weights(const float* w, int64_t rows, int64_t K, uint8_t* q,
+                                       float* scales, hipStream_t stream);
+hipError_t launch_quantize_fp8_activations(const uint16_t* x, int64_t rows, int64_t K, float ub,
+                                           uint8_t* q, float* scales, hipStream_t stream);
 // bf16 [rows, K] -> 16 x 128 tiles in MFMA step order (shared expert weights)
 hipError_t launch_pack_bf16(const uint16_t* src, int64_t rows, int64_t K, uint16_t* dst,
                             hipStream_t stream);
