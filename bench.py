@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s + TFLOP/s (prefill) and HBM GB/s (decode) on 1 MI355X"
 HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 DEFAULT_STEPS = {0: 500, 1: 500, 2: 40, 3: 40, 4: 10}
 DEFAULT_WARMUP = {0: 20, 1: 20, 2: 5, 3: 5, 4: 3}
 
@@ -48,8 +49,9 @@ def parse():
     ap.add_argument("--config", type=int, default=1, help="benchmark layer 0..4 (default 1)")
     ap.add_argument("--layers", type=int, default=None, help="independent layer copies to cycle")
     ap.add_argument("--path", default="auto", choices=["auto", "prefill", "decode", "hybrid"])
-    ap.add_argument("--experts", default="int4", choices=["int4", "bf16"],
-                    help="routed expert weights: int4 g128 (default) or bf16 (the baseline path)")
+    ap.add_argument("--experts", default="int4", choices=["int4", "bf16", "fp8"],
+                    help="routed expert weights: int4 g128 (default), bf16 (the baseline "
+                         "path) or fp8 row-wise (the fp8_mixed path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -88,6 +90,8 @@ def layer_weight_bytes(cfg, experts: str = "int4") -> int:
     g = 128
     if experts == "bf16":
         routed = cfg.E * 3 * cfg.h * cfg.d * 2
+    elif experts == "fp8":
+        routed = cfg.E * (3 * cfg.h * cfg.d + (2 * cfg.h + cfg.d) * 4)
     else:
         routed = cfg.E * 3 * (cfg.h * cfg.d // 2 + cfg.h * (cfg.d // g) * 4)
     shared = 3 * cfg.h * cfg.d * 2
@@ -102,6 +106,8 @@ def build_layer(cfg, dev, experts: str = "int4"):
     wr, b = W.gen_router(cfg)
     if experts == "bf16":
         ex = moe.Bf16Experts.empty(cfg.E, cfg.d, cfg.h, dev)
+    elif experts == "fp8":
+        ex = moe.Fp8Experts.empty(cfg.E, cfg.d, cfg.h, dev, W.FP8_ACT_UB)
     else:
         ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev)
     for e in range(cfg.E):
@@ -128,6 +134,8 @@ def stage_units(cfg, counts, experts: str = "int4"):
     touched = int((counts > 0).sum())
     if experts == "bf16":
         w13, w2 = 2 * h * d * 2, d * h * 2          # one routed expert's W1 + W3, its W2
+    elif experts == "fp8":
+        w13, w2 = 2 * (h * d + h * 4), d * h + d * 4  # fp8 codes + row scales
     else:
         w13 = 2 * (h * d // 2 + h * (d // g) * 4)   # one routed expert's W1 + W3 (int4 + scales)
         w2 = d * h // 2 + d * (h // g) * 4          # its W2
@@ -140,6 +148,11 @@ def stage_units(cfg, counts, experts: str = "int4"):
         "decode_up": (up_bytes, 4.0 * (P + T) * d * h),
         "decode_down": (down_bytes + T * d * 2, 2.0 * (P + T) * d * h),
         "combine": ((P + T) * d * 4 + T * d * 2, 2.0 * P * d),
+        # fp8 experts: x rows, then H's routed rows, read (bf16) and written (fp8 + scale)
+        "act_quant": (T * (d * 3 + 4) + P * (h * 3 + 4), 0.0),
+        # FLOPs of the up / down launches on fp8 matrix cores (routed rows), the rest bf16
+        "fp8_flops": {"grouped_up": 4.0 * P * d * h, "grouped_down": 2.0 * P * d * h}
+        if experts == "fp8" else {},
         "touched": touched,
         "step_bytes": touched * (w13 + w2) + 3 * h * d * 2 + E * d * 4 + 2 * T * d * 2,
     }
@@ -166,6 +179,11 @@ def cpu_baseline(layer, n_sample, dev, min_seconds=10.0):
             experts[e] = Bf16Expert(*(
                 W.gen_expert_weight(cfg, w, e, dev).to(torch.bfloat16).cpu()
                 .view(torch.int16).numpy().view(np.uint16).copy() for w in ("w1", "w3", "w2")))
+            continue
+        if layer["routed"] == "fp8":  # the oracle's own fp8 quantization of the same draws
+            experts[e] = native.fp8_expert(
+                *(W.gen_expert_weight(cfg, w, e, dev).cpu().numpy() for w in ("w1", "w3", "w2")),
+                W.FP8_ACT_UB)
             continue
         parts = []  # oracle's own quantization of the same draws
         for w in ("w1", "w3", "w2"):
@@ -224,7 +242,8 @@ def main() -> int:
           file=sys.stderr, flush=True)
 
     layers = [build_layer(cfg0.with_(seed=s), dev, args.experts) for s in range(nlayers)]
-    ws = moe.alloc_workspace(cfg0.T, cfg0.d, cfg0.E, cfg0.h, cfg0.top_k, dev)
+    ws = moe.alloc_workspace(cfg0.T, cfg0.d, cfg0.E, cfg0.h, cfg0.top_k, dev,
+                             fp8=args.experts == "fp8")
     y = torch.empty(cfg0.T, cfg0.d, dtype=torch.bfloat16, device=dev)
     ids = [torch.empty(cfg0.T, cfg0.top_k, dtype=torch.int32, device=dev) for _ in layers]
 
@@ -305,8 +324,11 @@ def main() -> int:
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
     else:
         achieved = flops / mean_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None}
+        # the launch's FLOPs at their own dtype's peak: fp8 routed rows, bf16 the rest
+        f8 = sum(units[i % nlayers]["fp8_flops"].get(dom, 0.0) for i in range(steps)) / steps
+        peak = flops / ((flops - f8) / BF16_MFMA_PEAK_TFLOPS + f8 / FP8_MFMA_PEAK_TFLOPS)
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None}
     roof["traffic"] = measured_traffic(dom, cfg0.name if args.experts == "int4" else None)
     if roof["traffic"] is not None:
         roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
@@ -339,10 +361,12 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8+bf16" if args.experts == "fp8" else "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg0.name}: T={cfg0.T} d={cfg0.d} E={cfg0.E}+1 shared "
                                f"h={cfg0.h} top_k={cfg0.top_k}, "
-                               + ("int4 g128" if args.experts == "int4" else "bf16")
+                               + {"int4": "int4 g128", "bf16": "bf16",
+                                  "fp8": f"fp8 row-wise (act ub {W.FP8_ACT_UB:g})"}[args.experts]
                                + " routed / bf16 shared",
                    "T": cfg0.T, "d": cfg0.d, "E": cfg0.E, "h": cfg0.h, "top_k": cfg0.top_k,
                    "parallelism": "single GPU"},

@@ -212,6 +212,36 @@ int moe_forward_bf16(const moe_dims *dims, const uint16_t *x, const float *route
                      float *topk_gates, int32_t path, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/* Routed experts in fp8 (OCP E4M3) with one fp32 scale per weight row: the
+ * fp8_mixed path of the lshu.cn page "Llama 4 单卡量化推理与选型指南"
+ * (sections "三条推理路径差异" and "量化环节"). Each matrix is written by
+ * moe_quantize_fp8_tiled and the experts are stacked:
+ *   w1q, w3q [E] x tiled [h, d]: E*h*d bytes   w1s, w3s: E*h fp32
+ *   w2q      [E] x tiled [d, h]: E*d*h bytes   w2s:      E*d fp32
+ * act_ub: the activation scale upper bound (finite, >= 0; 0: no bound). */
+typedef struct moe_experts_fp8 {
+    const uint8_t *w1q, *w3q, *w2q;
+    const float *w1s, *w3s, *w2s;
+    float act_ub;
+} moe_experts_fp8;
+
+/* Bytes of device workspace moe_forward_fp8 needs for `dims` (0 if invalid):
+ * the moe_forward workspace plus the fp8 activation rows and their scales. */
+size_t moe_forward_fp8_workspace_bytes(const moe_dims *dims);
+
+/* moe_forward_path with fp8 routed experts. Each routed expert computes, as
+ * on the page: x_t quantized per row (moe_quantize_fp8_rows with act_ub);
+ * a1 = bf16(xq W1q^T * sx * s1), a3 = bf16(xq W3q^T * sx * s3) (exact fp8
+ * products, fp32 sums); h = bf16(silu(a1) a3); h quantized per row the same
+ * way; out = bf16(hq W2q^T * sh * s2). The router, the shared bf16 expert,
+ * the gates, combine, paths, outputs and errors are those of moe_forward_path;
+ * workspace >= moe_forward_fp8_workspace_bytes(dims). */
+int moe_forward_fp8(const moe_dims *dims, const uint16_t *x, const float *router_w,
+                    const float *router_b, const moe_experts_fp8 *experts,
+                    const moe_shared_bf16 *shared, uint16_t *y, int32_t *topk_ids,
+                    float *topk_gates, int32_t path, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace moe_route alone needs (a prefix of the forward
  * workspace; 0 if dims are invalid; dims->h is ignored). */
 size_t moe_route_workspace_bytes(const moe_dims *dims);
@@ -251,8 +281,9 @@ enum moe_stage {
     MOE_STAGE_DOWN = 4,        /* K5 + shared down-projection */
     MOE_STAGE_COMBINE = 5,     /* gate-weighted sum + shared, bf16 out */
     MOE_STAGE_DECODE_UP = 6,   /* decode path: streaming up-projection */
-    MOE_STAGE_DECODE_DOWN = 7, /* decode path: streaming down-projection + combine */
-    MOE_STAGE_COUNT = 8
+    MOE_STAGE_DECODE_DOWN = 7, /* decode path: streaming down-projection */
+    MOE_STAGE_ACT_QUANT = 8,   /* fp8 experts: per-row fp8 quantization of x and H */
+    MOE_STAGE_COUNT = 9
 };
 
 int moe_profile_enable(int on);

@@ -57,6 +57,12 @@ class _ExpertsBf16(ctypes.Structure):
     _fields_ = [("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
 
 
+class _ExpertsFp8(ctypes.Structure):
+    _fields_ = [("w1q", ctypes.c_void_p), ("w3q", ctypes.c_void_p), ("w2q", ctypes.c_void_p),
+                ("w1s", ctypes.c_void_p), ("w3s", ctypes.c_void_p), ("w2s", ctypes.c_void_p),
+                ("act_ub", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -92,6 +98,12 @@ def lib() -> ctypes.CDLL:
         fwd_bf16 = list(fwd)
         fwd_bf16[4] = ctypes.POINTER(_ExpertsBf16)
         L.moe_forward_bf16.argtypes = fwd_bf16 + [i32, P, sz, P]
+        fwd_fp8 = list(fwd)
+        fwd_fp8[4] = ctypes.POINTER(_ExpertsFp8)
+        L.moe_forward_fp8.argtypes = fwd_fp8 + [i32, P, sz, P]
+        L.moe_forward_fp8.restype = ctypes.c_int
+        L.moe_forward_fp8_workspace_bytes.argtypes = [ctypes.POINTER(_Dims)]
+        L.moe_forward_fp8_workspace_bytes.restype = sz
         L.moe_quantize_fp8_tiled.argtypes = [P, i64, i64, P, P, P]
         L.moe_quantize_fp8_tiled.restype = ctypes.c_int
         L.moe_quantize_fp8_rows.argtypes = [P, i64, i64, ctypes.c_float, P, P, P]
@@ -273,16 +285,19 @@ class Int4Experts:
 
 # ----------------------------------------------------------------- forward
 
-def workspace_bytes(T: int, d: int, E: int, h: int, top_k: int) -> int:
+def workspace_bytes(T: int, d: int, E: int, h: int, top_k: int, fp8: bool = False) -> int:
+    """Workspace bytes of the forward (``fp8``: with fp8 routed experts)."""
     dims = _dims(T, d, E, h, top_k)
-    n = lib().moe_forward_workspace_bytes(ctypes.byref(dims))
+    fn = lib().moe_forward_fp8_workspace_bytes if fp8 else lib().moe_forward_workspace_bytes
+    n = fn(ctypes.byref(dims))
     if n == 0:
         raise ValueError(f"invalid layer dims T={T} d={d} E={E} h={h} top_k={top_k}")
     return n
 
 
-def alloc_workspace(T: int, d: int, E: int, h: int, top_k: int, device) -> torch.Tensor:
-    return torch.empty(workspace_bytes(T, d, E, h, top_k), dtype=torch.uint8, device=device)
+def alloc_workspace(T: int, d: int, E: int, h: int, top_k: int, device,
+                    fp8: bool = False) -> torch.Tensor:
+    return torch.empty(workspace_bytes(T, d, E, h, top_k, fp8), dtype=torch.uint8, device=device)
 
 
 @dataclass
@@ -325,12 +340,66 @@ class Bf16Experts:
         return _ExpertsBf16(self.w1.data_ptr(), self.w3.data_ptr(), self.w2.data_ptr())
 
 
+@dataclass
+class Fp8Experts:
+    """Stacked routed experts in fp8 E4M3 with one fp32 scale per weight row (the
+    fp8_mixed path), codes in the tiled order of ``quantize_fp8``; ``act_ub`` bounds
+    the activation row scales."""
+
+    w1q: torch.Tensor  # uint8 [E, h, d]
+    w3q: torch.Tensor  # uint8 [E, h, d]
+    w2q: torch.Tensor  # uint8 [E, d, h]
+    w1s: torch.Tensor  # fp32  [E, h]
+    w3s: torch.Tensor  # fp32  [E, h]
+    w2s: torch.Tensor  # fp32  [E, d]
+    act_ub: float
+
+    @property
+    def E(self) -> int:
+        return self.w1q.shape[0]
+
+    @property
+    def h(self) -> int:
+        return self.w1q.shape[1]
+
+    @property
+    def d(self) -> int:
+        return self.w2q.shape[1]
+
+    @staticmethod
+    def empty(E: int, d: int, h: int, device, act_ub: float) -> "Fp8Experts":
+        u8, f32 = torch.uint8, torch.float32
+        return Fp8Experts(
+            torch.empty(E, h, d, dtype=u8, device=device),
+            torch.empty(E, h, d, dtype=u8, device=device),
+            torch.empty(E, d, h, dtype=u8, device=device),
+            torch.empty(E, h, dtype=f32, device=device),
+            torch.empty(E, h, dtype=f32, device=device),
+            torch.empty(E, d, dtype=f32, device=device),
+            float(act_ub))
+
+    def quantize_expert(self, e: int, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor):
+        """Quantize one expert's fp32 weights (on the GPU) into slot ``e`` (tiled)."""
+        quantize_fp8(w1, self.w1q[e], self.w1s[e])
+        quantize_fp8(w3, self.w3q[e], self.w3s[e])
+        quantize_fp8(w2, self.w2q[e], self.w2s[e])
+
+    def _struct(self) -> _ExpertsFp8:
+        for name in ("w1q", "w3q", "w2q"):
+            _need(getattr(self, name), name, torch.uint8)
+        for name in ("w1s", "w3s", "w2s"):
+            _need(getattr(self, name), name, torch.float32)
+        return _ExpertsFp8(*(getattr(self, n).data_ptr() for n in
+                             ("w1q", "w3q", "w2q", "w1s", "w3s", "w2s")), float(self.act_ub))
+
+
 def forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor],
             experts, shared, top_k: int, path: str = "auto",
             y: Optional[torch.Tensor] = None, topk_ids: Optional[torch.Tensor] = None,
             topk_gates: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The MoE layer: y bf16 [T, d]. ``experts``: ``Int4Experts`` or ``Bf16Experts``;
+    """The MoE layer: y bf16 [T, d]. ``experts``: ``Int4Experts``, ``Bf16Experts`` or
+    ``Fp8Experts``;
     ``shared`` = (S1 [h, d], S3 [h, d], S2 [d, h]) bf16, packed by ``pack_shared``."""
     _need(x, "x", torch.bfloat16)
     T, d = x.shape
@@ -351,12 +420,18 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Te
         _need(topk_ids, "topk_ids", torch.int32, (T, top_k))
     if topk_gates is not None:
         _need(topk_gates, "topk_gates", torch.float32, (T, top_k))
+    fp8 = isinstance(experts, Fp8Experts)
     if workspace is None:
-        workspace = alloc_workspace(T, d, E, h, top_k, x.device)
+        workspace = alloc_workspace(T, d, E, h, top_k, x.device, fp8)
     dims = _dims(T, d, E, h, top_k)
     ex = experts._struct()
     sh = _Shared(s1.data_ptr(), s3.data_ptr(), s2.data_ptr())
-    entry = lib().moe_forward_bf16 if isinstance(experts, Bf16Experts) else lib().moe_forward_path
+    if fp8:
+        entry = lib().moe_forward_fp8
+    elif isinstance(experts, Bf16Experts):
+        entry = lib().moe_forward_bf16
+    else:
+        entry = lib().moe_forward_path
     _check(entry(
         ctypes.byref(dims), _ptr(x), _ptr(router_w), _ptr(router_b), ctypes.byref(ex),
         ctypes.byref(sh), _ptr(y), _ptr(topk_ids), _ptr(topk_gates), PATHS[path],
@@ -422,7 +497,7 @@ def unpack_int4(q: torch.Tensor) -> torch.Tensor:
 
 # ------------------------------------------------------------------ timing
 
-STAGE_COUNT = 8
+STAGE_COUNT = 9
 
 
 def profile_enable(on: bool = True) -> None:

@@ -47,6 +47,7 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
     size_t partials, logits, ids, gates, counts, offsets, tile_base, perm, inv, chunks, nchunks,
         routing_end, x_perm, H, O, total;
+    size_t xq, sxq, hq, shq, total_fp8;  // fp8 experts: quantized x and H rows, row scales
     int slices;
     int max_chunks;
 };
@@ -85,6 +86,11 @@ Layout layout(const moe_dims& d) {
     L.H = take((P + T) * static_cast<size_t>(d.h) * 2);
     L.O = take((P + T) * static_cast<size_t>(d.d) * 4);
     L.total = off;
+    L.xq = take(T * static_cast<size_t>(d.d));
+    L.sxq = take(T * 4);
+    L.hq = take(P * static_cast<size_t>(d.h));
+    L.shq = take(P * 4);
+    L.total_fp8 = off;
     return L;
 }
 
@@ -213,7 +219,7 @@ int device_ok() {
 
 int check_forward_args(const moe_dims* dims, const uint16_t* x, const float* router_w,
                        const float* router_b, void* workspace, size_t workspace_bytes,
-                       bool routing_only = false) {
+                       bool routing_only = false, bool fp8 = false) {
     CHECK(check_dims(dims));
     CHECK(check_ptr(x, "x"));
     CHECK(check_ptr(router_w, "router_w"));
@@ -221,7 +227,7 @@ int check_forward_args(const moe_dims* dims, const uint16_t* x, const float* rou
     if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
     if (!aligned(workspace, kAlign)) return fail(MOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
     const Layout L = layout(*dims);
-    const size_t need = routing_only ? L.routing_end : L.total;
+    const size_t need = routing_only ? L.routing_end : (fp8 ? L.total_fp8 : L.total);
     if (workspace_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
     return MOE_OK;
@@ -438,17 +444,28 @@ int moe_route(const moe_dims* dims, const uint16_t* x, const float* router_w,
     return MOE_OK;
 }
 
-// The forward for int4 (ex4) or bf16 (exb) routed experts; exactly one is set.
+// The forward for int4 (ex4), bf16 (exb) or fp8 (ex8) routed experts; exactly one is set.
 static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* router_w,
                         const float* router_b, const moe_experts_int4* ex4,
-                        const moe_experts_bf16* exb, const moe_shared_bf16* sh, uint16_t* y,
-                        int32_t* topk_ids, float* topk_gates, int32_t path, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        const moe_experts_bf16* exb, const moe_experts_fp8* ex8,
+                        const moe_shared_bf16* sh, uint16_t* y, int32_t* topk_ids,
+                        float* topk_gates, int32_t path, void* workspace, size_t workspace_bytes,
+                        void* stream) {
     g_last_error.clear();
-    CHECK(check_forward_args(dims, x, router_w, router_b, workspace, workspace_bytes));
-    if (!ex4 && !exb) return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
+    CHECK(check_forward_args(dims, x, router_w, router_b, workspace, workspace_bytes, false,
+                             ex8 != nullptr));
+    if (!ex4 && !exb && !ex8) return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
     if (!sh) return fail(MOE_ERR_INVALID_ARG, "shared is NULL");
-    if (ex4) {
+    if (ex8) {
+        CHECK(check_ptr(ex8->w1q, "experts->w1q", 4));
+        CHECK(check_ptr(ex8->w3q, "experts->w3q", 4));
+        CHECK(check_ptr(ex8->w2q, "experts->w2q", 4));
+        CHECK(check_ptr(ex8->w1s, "experts->w1s", 4));
+        CHECK(check_ptr(ex8->w3s, "experts->w3s", 4));
+        CHECK(check_ptr(ex8->w2s, "experts->w2s", 4));
+        if (!(ex8->act_ub >= 0.f) || ex8->act_ub > 3.0e38f)
+            return fail(MOE_ERR_INVALID_ARG, "experts->act_ub must be finite and >= 0");
+    } else if (ex4) {
         CHECK(check_ptr(ex4->w1q, "experts->w1q"));
         CHECK(check_ptr(ex4->w3q, "experts->w3q"));
         CHECK(check_ptr(ex4->w2q, "experts->w2q"));
@@ -486,9 +503,24 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
                                     (path == MOE_PATH_AUTO && P < kHybridAvgPairs * d.E));
     const int small_rows = decode ? -1 : (hybrid ? kHybridRows : 0);
     uint16_t* x_perm = reinterpret_cast<uint16_t*>(base + L.x_perm);
+    uint8_t* xq = ex8 ? reinterpret_cast<uint8_t*>(base + L.xq) : nullptr;
+    float* sxq = ex8 ? reinterpret_cast<float*>(base + L.sxq) : nullptr;
+    uint8_t* hq = ex8 ? reinterpret_cast<uint8_t*>(base + L.hq) : nullptr;
+    float* shq = ex8 ? reinterpret_cast<float*>(base + L.shq) : nullptr;
     // the interleaved copy of x feeds only the streaming kernel's int4 experts
     CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates,
                       (decode || hybrid) && ex4 ? x_perm : nullptr, small_rows, s));
+    // fp8 experts: quantize x per row (the routed rows' A operand); H's routed
+    // rows follow once the up-projections have written them
+    if (ex8)
+        CHECK(timed(MOE_STAGE_ACT_QUANT, s, "fp8 x quantize launch", [&] {
+            return moe::launch_quantize_fp8_activations(x, d.T, d.d, ex8->act_ub, xq, sxq, s);
+        }));
+    auto quantize_h = [&] {
+        return timed(MOE_STAGE_ACT_QUANT, s, "fp8 H quantize launch", [&] {
+            return moe::launch_quantize_fp8_activations(H, P, d.h, ex8->act_ub, hq, shq, s);
+        });
+    };
 
     // streaming projections over the chunk list: every group (decode path) or
     // the small routed experts (hybrid path)
@@ -510,6 +542,13 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
             a.ws0 = ex4->w1s;
             a.wq1 = ex4->w3q;
             a.ws1 = ex4->w3s;
+        } else if (ex8) {
+            a.wf0 = ex8->w1q;
+            a.wf1 = ex8->w3q;
+            a.wfs0 = ex8->w1s;
+            a.wfs1 = ex8->w3s;
+            a.a8 = xq;
+            a.a8s = sxq;
         } else {
             a.wb0 = exb->w1;
             a.wb1 = exb->w3;
@@ -536,6 +575,11 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         if (ex4) {
             a.wq0 = ex4->w2q;
             a.ws0 = ex4->w2s;
+        } else if (ex8) {
+            a.wf0 = ex8->w2q;
+            a.wfs0 = ex8->w2s;
+            a.a8 = hq;
+            a.a8s = shq;
         } else {
             a.wb0 = exb->w2;
         }
@@ -551,9 +595,10 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
     if (decode) {
         // bf16 chunks are split four ways: the shared expert's, at the head of
         // the list, or every chunk when the routed experts are bf16
-        const int split = ex4 ? static_cast<int>((d.T + moe::kDecodeRows - 1) / moe::kDecodeRows)
-                              : L.max_chunks;
+        const int split = exb ? L.max_chunks
+                              : static_cast<int>((d.T + moe::kDecodeRows - 1) / moe::kDecodeRows);
         CHECK(stream_up(L.max_chunks, split));
+        if (ex8) CHECK(quantize_h());
         CHECK(stream_down(L.max_chunks, split));
     } else {
         moe::GroupedGemmArgs g{};
@@ -574,6 +619,13 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
             g.ws0 = ex4->w1s;
             g.wq1 = ex4->w3q;
             g.ws1 = ex4->w3s;
+        } else if (ex8) {
+            g.wf0 = ex8->w1q;
+            g.wf1 = ex8->w3q;
+            g.wfs0 = ex8->w1s;
+            g.wfs1 = ex8->w3s;
+            g.a8 = xq;
+            g.a8s = sxq;
         } else {
             g.wb0 = exb->w1;
             g.wb1 = exb->w3;
@@ -582,8 +634,9 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         g.sh1 = sh->s3;
         g.h_out = H;
         CHECK(timed(MOE_STAGE_UP, s, "grouped up launch", [&] { return moe::launch_grouped_up(g, s); }));
-        const int hsplit = ex4 ? 0 : static_cast<int>(hybrid_chunks);
+        const int hsplit = exb ? static_cast<int>(hybrid_chunks) : 0;
         if (hybrid) CHECK(stream_up(static_cast<int>(hybrid_chunks), hsplit));
+        if (ex8) CHECK(quantize_h());
 
         g.a = H;
         g.K = d.h;
@@ -592,8 +645,14 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         g.ws0 = ex4 ? ex4->w2s : nullptr;
         g.wq1 = nullptr;
         g.ws1 = nullptr;
-        g.wb0 = ex4 ? nullptr : exb->w2;
+        g.wb0 = exb ? exb->w2 : nullptr;
         g.wb1 = nullptr;
+        g.wf0 = ex8 ? ex8->w2q : nullptr;
+        g.wf1 = nullptr;
+        g.wfs0 = ex8 ? ex8->w2s : nullptr;
+        g.wfs1 = nullptr;
+        g.a8 = hq;
+        g.a8s = shq;
         g.sh0 = sh->s2;
         g.sh1 = nullptr;
         g.h_out = nullptr;
@@ -618,7 +677,7 @@ int moe_forward_path(const moe_dims* dims, const uint16_t* x, const float* route
         g_last_error.clear();
         return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
     }
-    return forward_impl(dims, x, router_w, router_b, experts, nullptr, shared, y, topk_ids,
+    return forward_impl(dims, x, router_w, router_b, experts, nullptr, nullptr, shared, y, topk_ids,
                         topk_gates, path, workspace, workspace_bytes, stream);
 }
 
@@ -631,7 +690,27 @@ int moe_forward_bf16(const moe_dims* dims, const uint16_t* x, const float* route
         g_last_error.clear();
         return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
     }
-    return forward_impl(dims, x, router_w, router_b, nullptr, experts, shared, y, topk_ids,
+    return forward_impl(dims, x, router_w, router_b, nullptr, experts, nullptr, shared, y, topk_ids,
+                        topk_gates, path, workspace, workspace_bytes, stream);
+}
+
+size_t moe_forward_fp8_workspace_bytes(const moe_dims* dims) {
+    const std::string saved = g_last_error;
+    if (check_dims(dims) != MOE_OK) return 0;
+    g_last_error = saved;
+    return layout(*dims).total_fp8;
+}
+
+int moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float* router_w,
+                    const float* router_b, const moe_experts_fp8* experts,
+                    const moe_shared_bf16* shared, uint16_t* y, int32_t* topk_ids,
+                    float* topk_gates, int32_t path, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    if (!experts) {
+        g_last_error.clear();
+        return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
+    }
+    return forward_impl(dims, x, router_w, router_b, nullptr, nullptr, experts, shared, y, topk_ids,
                         topk_gates, path, workspace, workspace_bytes, stream);
 }
 
@@ -678,7 +757,8 @@ int moe_profile_read(double* ms, int64_t* launches, int n) {
 
 const char* moe_stage_name(int stage) {
     static const char* names[MOE_STAGE_COUNT] = {"router", "topk", "dispatch", "grouped_up",
-                                                 "grouped_down", "combine", "decode_up", "decode_down"};
+                                                 "grouped_down", "combine", "decode_up", "decode_down",
+                                                 "act_quant"};
     return (stage >= 0 && stage < MOE_STAGE_COUNT) ? names[stage] : "unknown";
 }
 

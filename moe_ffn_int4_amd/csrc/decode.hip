@@ -171,9 +171,53 @@ __device__ __forceinline__ void compute_shared(const SharedSlot& sl, f32x4& acc0
     }
 }
 
+// fp8 routed experts: per 128-wide group a lane holds 32 weight bytes of its
+// feature's row and the same 32 columns of its A row. Load j (j = 0, 1) of a
+// wave reads 1 KB of the 2 KB tile (steps 2j, 2j + 1): lane (l16, kq) takes
+// step 2j + kq / 2, bytes 16 (kq % 2) .. + 15, i.e. columns
+// 32 (2j + kq / 2) + 16 (kq % 2) .. + 15 of the group. MFMA step i pairs byte
+// 8i .. 8i + 7 of both operands; the four kq lanes of a feature together cover
+// the group's 128 columns once, so the sum is the same dot product.
+struct Fp8Slot {
+    uint4 w0[2], w1[2];
+    uint4 a[2];
+};
+
+template <bool UP>
+__device__ __forceinline__ void load_fp8(Fp8Slot& sl, const uint8_t* q0, const uint8_t* q1,
+                                         const uint8_t* arow, int g, int boff0, int aoff0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        sl.w0[j] = ld_stream(q0 + g * 2048 + boff0 + j * 1024);
+        if (UP) sl.w1[j] = ld_stream(q1 + g * 2048 + boff0 + j * 1024);
+        sl.a[j] = *reinterpret_cast<const uint4*>(arow + g * kGroup + aoff0 + j * 64);
+    }
+}
+
+template <bool UP>
+__device__ __forceinline__ void compute_fp8(const Fp8Slot& sl, f32x4& acc0, f32x4& acc1) {
+    typedef long long2v __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const long2v av = __builtin_bit_cast(long2v, sl.a[j]);
+        const long2v b0 = __builtin_bit_cast(long2v, sl.w0[j]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(av[h], b0[h], acc0, 0, 0, 0);
+        if (UP) {
+            const long2v b1 = __builtin_bit_cast(long2v, sl.w1[j]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(av[h], b1[h], acc1, 0, 0, 0);
+        }
+    }
+}
+
 // DR / DS: groups kept in flight ahead of the one being computed, for int4
 // (routed) and bf16 (shared) weights
-template <bool UP, int DR, int DS, int DL>
+// F8: the routed experts are fp8 (a separate instantiation, so the int4 one
+// keeps its register budget)
+template <bool UP, int DR, int DS, int DL, bool F8>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     // routed chunks of at most a.lds_rows rows keep their A rows in LDS
     extern __shared__ __attribute__((aligned(16))) uint16_t a_lds[];
@@ -194,12 +238,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const int4 ch = a.chunks[c];
     const int group = ch.x, row0 = ch.y, nrows = ch.z;
     const bool routed = group < a.E;
-    const bool int4 = routed && !a.wb0;  // otherwise bf16 weights (shared, or bf16 routed)
-    if (int4 && blockIdx.y >= a.max_chunks) return;
+    const bool fp8 = F8 && routed;
+    const bool int4 = !F8 && routed && !a.wb0;  // otherwise bf16 weights (shared, or bf16 routed)
+    const bool narrow = int4 || fp8;              // one wave per 16 features, whole reduction
+    if (narrow && blockIdx.y >= a.max_chunks) return;
     const int64_t K = a.K, N = a.N;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kq = lane >> 4;
-    const int64_t n = static_cast<int64_t>(blockIdx.x) * 64 + (int4 ? wave : sub) * 16 + l16;  // B column
+    const int64_t n = static_cast<int64_t>(blockIdx.x) * 64 + (narrow ? wave : sub) * 16 + l16;  // B column
     const int ng = static_cast<int>(K / kGroup);
 
     // A row of MFMA row l16: int4 routed experts read the interleaved copy, bf16
@@ -215,7 +261,49 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const uint16_t* arow = (int4 ? a.a_perm : a.a) + src * K + (int4 ? kq * 32 : kq * 8);
 
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    if (int4 && nrows <= a.lds_rows) {
+    if (fp8) {
+        constexpr int D = DR;
+        constexpr int U = D + 1;
+        const int64_t mat = static_cast<int64_t>(group) * N * K;
+        const int64_t tb = (n >> 4) * ng * 2048 + l16 * 32;  // this feature's row in its tiles
+        const uint8_t* q0 = a.wf0 + mat + tb;
+        const uint8_t* q1 = UP ? a.wf1 + mat + tb : nullptr;
+        const int boff0 = (kq >> 1) * 512 + (kq & 1) * 16;
+        const int aoff0 = (kq >> 1) * 32 + (kq & 1) * 16;
+        const uint8_t* a8row = a.a8 + src * K;
+        Fp8Slot sl[U];
+#pragma unroll
+        for (int p = 0; p < D; ++p) load_fp8<UP>(sl[p], q0, q1, a8row, min(p, ng - 1), boff0, aoff0);
+        const int full = ng - ng % U;
+        for (int g0 = 0; g0 < full; g0 += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                load_fp8<UP>(sl[(u + D) % U], q0, q1, a8row, min(g0 + u + D, ng - 1), boff0, aoff0);
+                compute_fp8<UP>(sl[u], acc0, acc1);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < D; ++u)
+            if (u < ng - full) compute_fp8<UP>(sl[u], acc0, acc1);
+        // scale by both row scales; bf16 where the fp8 products return bf16
+        const float w0s = a.wfs0[static_cast<int64_t>(group) * N + n];
+        const float w1s = UP ? a.wfs1[static_cast<int64_t>(group) * N + n] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int mr = kq * 4 + r;
+            if (mr >= nrows) continue;
+            const int64_t orow = row0 + mr;
+            const float sa = a.a8s[UP ? a.perm[orow] / a.top_k : orow];
+            if (UP) {
+                const float g = bf16_to_f32(f32_to_bf16(acc0[r] * sa * w0s));
+                const float u = bf16_to_f32(f32_to_bf16(acc1[r] * sa * w1s));
+                a.h_out[orow * N + n] = f32_to_bf16(siluf_(g) * u);
+            } else {
+                a.o_out[orow * N + n] = bf16_to_f32(f32_to_bf16(acc0[r] * sa * w0s));
+            }
+        }
+        return;
+    } else if (int4 && nrows <= a.lds_rows) {
         // Stage the chunk's A rows (interleaved copies) in LDS once; the weight
         // ring then carries only weights and scales, and A comes from LDS.
         constexpr int D = DL;
@@ -361,7 +449,8 @@ static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, int shar
     size_t lds = a.lds_rows > 0 ? static_cast<size_t>(a.lds_rows) * (a.K + 8) * 2 : 0;
     lds = lds > kReduceLdsBytes ? lds : kReduceLdsBytes;
     dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks + 3 * shared_chunks));
-    hipLaunchKernelGGL((decode_kernel<UP, DR, DS, DL>), grid, dim3(NT), lds, stream, a);
+    if (a.wf0) hipLaunchKernelGGL((decode_kernel<UP, DR, DS, DL, true>), grid, dim3(NT), lds, stream, a);
+    else hipLaunchKernelGGL((decode_kernel<UP, DR, DS, DL, false>), grid, dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
 

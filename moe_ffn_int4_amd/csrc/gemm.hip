@@ -303,6 +303,153 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
     }
 }
 
+// Routed tiles of fp8 experts: A is the tile's fp8 activation rows (x_q by
+// token for up, H_q by slot for down; quantized per row beforehand), B the
+// expert's fp8 weights, v_mfma_f32_16x16x32_fp8_fp8 (exact fp8 products, fp32
+// sums). Same tile, waves and pipeline as gemm_tile; one 16-row x 32-column
+// sub-tile of either operand is 512 B in fragment order (lane l's 8 bytes,
+// row l % 16, columns 8 (l / 16).., at 8 l), so staging writes and fragment
+// reads are both contiguous. The epilogue scales by both row scales and
+// rounds to bf16 where the fp8 matmul of the pages returns bf16: the two
+// up-projections, then the SwiGLU product (bf16 H); down: the expert output.
+template <bool UP>
+__device__ __forceinline__ void gemm_tile_fp8(const GroupedGemmArgs& a, const Tile& tile, int nt,
+                                              uint8_t* lds) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int SUB = 512;                  // bytes per 16 x 32 fp8 sub-tile
+    constexpr int ASUB = BM / 16;             // 8 A sub-tiles
+    constexpr int STAGE_BYTES = (ASUB + 16) * SUB;
+    const int64_t K = a.K, N = a.N;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int wm = wid >> 1, wn = wid & 1;
+    const int r16 = lane & 15, q4 = lane >> 4;
+    const int64_t n0 = static_cast<int64_t>(nt) * (UP ? BN / 2 : BN);
+    const int64_t ng = K / kGroup;
+    const int steps = static_cast<int>(K / BK);
+
+    // ---- A: this wave stages sub-tiles 2 wid, 2 wid + 1 (rows 32 wid + 16 i + r16)
+    const uint8_t* arow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        int r = 32 * wid + 16 * i + r16;
+        r = r < tile.nrows ? r : tile.nrows - 1;
+        const int64_t s = tile.row0 + r;
+        const int64_t src = UP ? a.perm[s] / a.top_k : s;
+        arow[i] = a.a8 + src * K + 8 * q4;
+    }
+    // ---- B: this wave stages sub-tiles 4 wid .. 4 wid + 3 (B rows 16 j + r16)
+    const uint8_t* brow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int br = 16 * (4 * wid + i) + r16;
+        int64_t bn = UP ? n0 + (br & 127) : n0 + br;
+        bn = bn < N ? bn : N - 1;
+        const uint8_t* m = ((UP && br >= 128) ? a.wf1 : a.wf0) + static_cast<int64_t>(tile.group) * N * K;
+        brow[i] = m + (bn >> 4) * ng * 2048 + (bn & 15) * 32 + 8 * q4;  // + group*2048 + step*512
+    }
+
+    u32x2 ra0[2], rb0[4], ra1[2], rb1[4];
+    auto load_step = [&](u32x2 (&ra)[2], u32x2 (&rb)[4], int k) __attribute__((always_inline)) {
+        k = k < steps ? k : steps - 1;
+        const int64_t k0 = static_cast<int64_t>(k) * BK;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x2*>(arow[i] + k0);
+        const int64_t boff = (k0 / kGroup) * 2048 + (k & 3) * 512;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rb[i] = *reinterpret_cast<const u32x2*>(brow[i] + boff);
+    };
+    auto store_step = [&](const u32x2 (&ra)[2], const u32x2 (&rb)[4], int stage)
+                          __attribute__((always_inline)) {
+        uint8_t* st = lds + stage * STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            *reinterpret_cast<u32x2*>(st + (2 * wid + i) * SUB + lane * 8) = ra[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x2*>(st + (ASUB + 4 * wid + i) * SUB + lane * 8) = rb[i];
+    };
+
+    f32x4 acc[4][8];
+    int sb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sb[j] = UP ? ((j < 4) ? wn * 4 + j : 8 + wn * 4 + (j - 4)) : wn * 8 + j;
+    auto mfma_step = [&](int stage, auto first) __attribute__((always_inline)) {
+        constexpr bool FIRST = decltype(first)::value;
+        const uint8_t* st = lds + stage * STAGE_BYTES;
+        long fa[4], fb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fb[j] = *reinterpret_cast<const long*>(st + (ASUB + sb[j]) * SUB + lane * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const long*>(st + (wm * 4 + i) * SUB + lane * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                    fa[i], fb[j], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+    };
+
+    load_step(ra0, rb0, 0);
+    load_step(ra1, rb1, 1);
+    store_step(ra0, rb0, 0);
+    __syncthreads();
+    load_step(ra0, rb0, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(0, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    store_step(ra1, rb1, 1);
+    __syncthreads();
+    int k = 1;
+    for (; k + 1 < steps; k += 2) {
+        load_step(ra1, rb1, k + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(1, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        store_step(ra0, rb0, 0);
+        __syncthreads();
+        load_step(ra0, rb0, k + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(0, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        store_step(ra1, rb1, 1);
+        __syncthreads();
+    }
+    mfma_step(1, std::false_type{});
+
+    // ---- epilogue: D[row][col], row = 4 * lq + r inside a 16 x 16 sub-tile, col = l16
+    const int l16 = lane & 15, lq = lane >> 4;
+    const float* ws0 = a.wfs0 + static_cast<int64_t>(tile.group) * N;
+    const float* ws1 = UP ? a.wfs1 + static_cast<int64_t>(tile.group) * N : nullptr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = wm * 64 + i * 16 + lq * 4 + r;
+            if (row >= tile.nrows) continue;
+            const int64_t orow = tile.row0 + row;
+            const float sa = a.a8s[UP ? a.perm[orow] / a.top_k : orow];
+            if (UP) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t col = n0 + wn * 64 + j * 16 + l16;
+                    const float g = bf16_to_f32(f32_to_bf16(acc[i][j][r] * sa * ws0[col]));
+                    const float u = bf16_to_f32(f32_to_bf16(acc[i][j + 4][r] * sa * ws1[col]));
+                    a.h_out[orow * N + col] = f32_to_bf16(siluf_(g) * u);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t col = n0 + wn * 128 + j * 16 + l16;
+                    if (col < N) a.o_out[orow * N + col] = bf16_to_f32(f32_to_bf16(acc[i][j][r] * sa * ws0[col]));
+                }
+            }
+        }
+    }
+}
+
 template <bool UP>
 __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(GroupedGemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 3 stages of [A | B]
@@ -325,7 +472,8 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(GroupedGemmArgs a) 
 
     Tile tile;
     if (!find_tile(a, mt, tile)) return;
-    if (tile.group < a.E && !a.wb0) gemm_tile<UP, true>(a, tile, nt, lds);
+    if (tile.group < a.E && a.wf0) gemm_tile_fp8<UP>(a, tile, nt, lds);
+    else if (tile.group < a.E && !a.wb0) gemm_tile<UP, true>(a, tile, nt, lds);
     else gemm_tile<UP, false>(a, tile, nt, lds);
 }
 

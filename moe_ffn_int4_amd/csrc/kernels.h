@@ -88,6 +88,12 @@ struct GroupedGemmArgs {
     const uint16_t* sh1;     // up: S3
     const uint16_t* wb0;     // bf16 routed experts instead of int4 (null: int4):
     const uint16_t* wb1;     //   up: W1 / W3, down: W2 (tiled bf16 [E, N, K])
+    const uint8_t* wf0;      // fp8 routed experts instead of int4 (null: int4):
+    const uint8_t* wf1;      //   up: W1 / W3, down: W2 (tiled fp8 [E, N, K])
+    const float* wfs0;       //   their row scales [E, N]
+    const float* wfs1;
+    const uint8_t* a8;       // fp8 routed rows of A (up: x_q [T, d] by token;
+    const float* a8s;        //   down: H_q [P, h] by slot) and their row scales
     uint16_t* h_out;         // up: H [P + T, h] bf16
     float* o_out;            // down: O [P + T, d] fp32
 };
@@ -117,6 +123,12 @@ struct DecodeArgs {
     const uint16_t* sh1;
     const uint16_t* wb0;     // bf16 routed experts instead of int4 (null: int4)
     const uint16_t* wb1;
+    const uint8_t* wf0;      // fp8 routed experts instead of int4 (null: int4)
+    const uint8_t* wf1;
+    const float* wfs0;
+    const float* wfs1;
+    const uint8_t* a8;       // fp8 routed A rows (up: x_q by token, down: H_q by slot)
+    const float* a8s;
     uint16_t* h_out;
     float* o_out;
     int lds_rows;            // set by the launcher: routed chunks this small stage A in LDS

@@ -227,3 +227,162 @@ int oracle_moe_token_bf16(const double *x, int64_t d, int64_t h, int64_t E, int3
     for (int64_t m = 0; m < d; ++m) y[m] += o[m];
     return 0;
 }
+
+/* ------------------------------------------------------------ fp8 row-wise */
+/*
+ * The fp8_mixed path of the lshu.cn page "Llama 4 单卡量化推理与选型指南"
+ * (sections "三条推理路径差异" and "量化环节"): activations quantized per
+ * row to fp8 with an upper bound on the row scale, fp8 weights with one scale
+ * per row, the fp8 x fp8 product scaled by both row scales and returned in
+ * bf16. fp8 is OCP E4M3 (bias 7, 3 mantissa bits, largest finite 448,
+ * subnormal spacing 2^-9); conversion rounds to nearest, ties to even.
+ * A row's scale is min(max(max|v|, 1e-12), ub) / 448 (ub <= 0: no bound) and
+ * its codes are fp8(clamp(v / scale, -448, 448)), fp32 arithmetic.
+ * The same readings as the numpy form in fp8.py, written as plain loops.
+ */
+
+/* nearest E4M3 value to v, |v| <= 448: in the binade [2^e, 2^(e+1)) the
+ * spacing is 2^(e-3); below 2^-6 (subnormals) it is 2^-9 */
+static double fp8_round_value(double v)
+{
+    double a = fabs(v);
+    if (a == 0.0) return v;
+    int ex;
+    (void)frexp(a, &ex);  /* a = f * 2^ex with f in [0.5, 1): binade 2^(ex-1) */
+    int e = ex - 1;
+    if (e < -6) e = -6;
+    double spacing = ldexp(1.0, e - 3);
+    return copysign(nearbyint(a / spacing) * spacing, v);
+}
+
+/* bit pattern of an E4M3 value */
+static uint8_t fp8_bits(double v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a < ldexp(1.0, -6))                       /* exponent field 0 */
+        return (uint8_t)(sign | (uint8_t)(a / ldexp(1.0, -9)));
+    int ex;
+    double f = frexp(a, &ex);                     /* a = (2f) * 2^(ex-1), 2f in [1, 2) */
+    int mant = (int)((2.0 * f - 1.0) * 8.0);
+    return (uint8_t)(sign | (uint8_t)(((ex - 1 + 7) << 3) | mant));
+}
+
+double oracle_fp8_value(uint8_t c)
+{
+    int ef = (c >> 3) & 15, m = c & 7;
+    double v = ef == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, ef - 7);
+    return (c & 0x80) ? -v : v;
+}
+
+static void quantize_fp8_row(const float *v, int64_t K, float ub, uint8_t *q, float *scale)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < K; ++i) {
+        float a = fabsf(v[i]);
+        if (a > m) m = a;
+    }
+    if (m < 1e-12f) m = 1e-12f;
+    if (ub > 0.0f && m > ub) m = ub;
+    float s = m / 448.0f;
+    *scale = s;
+    for (int64_t i = 0; i < K; ++i) {
+        float t = v[i] / s;
+        if (t > 448.0f) t = 448.0f;
+        if (t < -448.0f) t = -448.0f;
+        q[i] = fp8_bits(fp8_round_value((double)t));
+    }
+}
+
+void oracle_quantize_fp8_rows(const float *w, int64_t rows, int64_t K, float ub,
+                              uint8_t *q, float *scales)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        quantize_fp8_row(w + r * K, K, ub, q + r * K, scales + r);
+}
+
+/* nearest bf16 value (ties to even) of the fp32 rounding of v */
+static double bf16_round_value(double v)
+{
+    float f = (float)v;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* bf16(sum_j fp8(a[j]) fp8(w[row][j]) * sa * sw[row]): the products are exact
+ * and so is their fp64 sum (every term is a multiple of 2^-18 below 2^18) */
+static double fp8_row_product(const uint8_t *a, float sa, const uint8_t *w, const float *sw,
+                              int64_t K, int64_t row)
+{
+    double acc = 0.0;
+    for (int64_t j = 0; j < K; ++j)
+        acc += oracle_fp8_value(a[j]) * oracle_fp8_value(w[row * K + j]);
+    return bf16_round_value(acc * (double)sa * (double)sw[row]);
+}
+
+/* One fp8 expert on one token (x: values of bf16 activations):
+ *   xq, sx = quantize(x);  a1[n] = bf16(xq.W1[n] sx s1[n]);  a3 likewise (W3)
+ *   u[n] = bf16(silu(a1[n]) a3[n]);  uq, su = quantize(u)
+ *   o[m] = bf16(uq.W2[m] su s2[m]) */
+void oracle_swiglu_fp8_token(const double *x, int64_t d, int64_t h,
+                             const uint8_t *q1, const float *s1,
+                             const uint8_t *q3, const float *s3,
+                             const uint8_t *q2, const float *s2, float ub,
+                             float *f32, uint8_t *codes, double *u, double *o)
+{
+    float sx, su;
+    for (int64_t j = 0; j < d; ++j) f32[j] = (float)x[j];
+    quantize_fp8_row(f32, d, ub, codes, &sx);
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < h; ++n) {
+        double a1 = fp8_row_product(codes, sx, q1, s1, d, n);
+        double a3 = fp8_row_product(codes, sx, q3, s3, d, n);
+        u[n] = bf16_round_value(silu(a1) * a3);
+    }
+    for (int64_t n = 0; n < h; ++n) f32[n] = (float)u[n];
+    quantize_fp8_row(f32, h, ub, codes, &su);
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < d; ++m)
+        o[m] = fp8_row_product(codes, su, q2, s2, h, m);
+}
+
+/*
+ * oracle_moe_token with fp8 routed experts: expert e's codes q1[e], q3[e]
+ * ([h, d] row-major), q2[e] ([d, h]) and row scales s1[e], s3[e] [h],
+ * s2[e] [d]; ub bounds the activation row scales. Router, gates and the bf16
+ * shared expert as in oracle_moe_token. scratch: f32 and codes of
+ * max(d, h) entries, u [h], o [d].
+ */
+int oracle_moe_token_fp8(const double *x, int64_t d, int64_t h, int64_t E, int32_t k,
+                         const float *wr, const float *bias,
+                         const uint8_t *const *q1, const float *const *s1,
+                         const uint8_t *const *q3, const float *const *s3,
+                         const uint8_t *const *q2, const float *const *s2, float ub,
+                         const uint16_t *sh1, const uint16_t *sh3, const uint16_t *sh2,
+                         const int32_t *forced_ids,
+                         float *logits, int32_t *ids, double *gates,
+                         float *f32, uint8_t *codes, double *u, double *o, double *y)
+{
+    oracle_router_token(x, wr, bias, E, d, logits);
+    if (forced_ids)
+        for (int32_t j = 0; j < k; ++j) ids[j] = forced_ids[j];
+    else
+        oracle_topk_token(logits, E, k, ids);
+
+    for (int64_t m = 0; m < d; ++m) y[m] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+        int32_t e = ids[j];
+        if (e < 0 || e >= E || !q1[e] || !q3[e] || !q2[e]) return -1;
+        gates[j] = sigmoid((double)logits[e]);
+        oracle_swiglu_fp8_token(x, d, h, q1[e], s1[e], q3[e], s3[e], q2[e], s2[e], ub,
+                                f32, codes, u, o);
+        for (int64_t m = 0; m < d; ++m) y[m] += gates[j] * o[m];
+    }
+    oracle_swiglu_bf16_token(x, d, h, sh1, sh3, sh2, u, o);
+    for (int64_t m = 0; m < d; ++m) y[m] += o[m];
+    return 0;
+}

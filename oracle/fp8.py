@@ -141,10 +141,11 @@ class Fp8Expert:
     def ffn(self, x) -> np.ndarray:
         """The expert on rows ``x`` (values of bf16 activations), fp64 result
         holding the bf16 expert output."""
+        ub = self.ub if self.ub > 0 else None  # a bound <= 0 means none
         x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
-        xq, sx = quantize_rows(x32, self.ub)
+        xq, sx = quantize_rows(x32, ub)
         a1 = _rowwise_product(xq, sx, self.q1, self.s1)
         a3 = _rowwise_product(xq, sx, self.q3, self.s3)
         h = bf16_round(silu(a1) * a3)
-        hq, sh = quantize_rows(h.astype(np.float32), self.ub)
+        hq, sh = quantize_rows(h.astype(np.float32), ub)
         return _rowwise_product(hq, sh, self.q2, self.s2)

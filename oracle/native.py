@@ -13,6 +13,7 @@ from typing import Callable, Optional, Sequence, Union
 
 import numpy as np
 
+from .fp8 import Fp8Expert
 from .moe import Bf16Expert, Int4Expert, MoEResult, _f64
 from .quantize import GROUP
 
@@ -61,6 +62,13 @@ def lib():
         L.oracle_moe_token_bf16.argtypes = ([P, i64, i64, i64, i32, P, P]
                                             + [P] * 3 + [P] * 3 + [P] + [P] * 6)
         L.oracle_moe_token_bf16.restype = ctypes.c_int
+        L.oracle_quantize_fp8_rows.argtypes = [P, i64, i64, ctypes.c_float, P, P]
+        L.oracle_quantize_fp8_rows.restype = None
+        L.oracle_fp8_value.argtypes = [ctypes.c_uint8]
+        L.oracle_fp8_value.restype = ctypes.c_double
+        L.oracle_moe_token_fp8.argtypes = ([P, i64, i64, i64, i32, P, P]
+                                           + [P] * 6 + [ctypes.c_float] + [P] * 3 + [P] + [P] * 8)
+        L.oracle_moe_token_fp8.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -78,6 +86,27 @@ def quantize_int4(w, group_size: int = GROUP):
     scales = np.empty(w.shape[:-1] + (K // group_size,), dtype=np.float32)
     lib().oracle_quantize_int4(_ptr(w), rows, K, group_size, _ptr(codes), _ptr(scales))
     return codes, scales
+
+
+def quantize_fp8_rows(w, ub: Optional[float] = None):
+    """C loop form of the fp8 row quantizer: ``(codes uint8, scales fp32 [rows])``;
+    ``ub`` None or <= 0: no bound on the row scale."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    K = w.shape[-1]
+    rows = w.size // K
+    codes = np.empty(w.shape, dtype=np.uint8)
+    scales = np.empty(w.shape[:-1], dtype=np.float32)
+    lib().oracle_quantize_fp8_rows(_ptr(w), rows, K, 0.0 if ub is None else float(ub),
+                                   _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def fp8_expert(w1, w3, w2, ub: float) -> Fp8Expert:
+    """An fp8 expert quantized by the C loops (same fields as ``Fp8Expert.from_fp32``)."""
+    q1, s1 = quantize_fp8_rows(w1)
+    q3, s3 = quantize_fp8_rows(w3)
+    q2, s2 = quantize_fp8_rows(w2)
+    return Fp8Expert(q1, s1, q3, s3, q2, s2, float(ub))
 
 
 def _bf16_bits(a) -> np.ndarray:
@@ -126,10 +155,23 @@ def moe_forward_per_token(x, wr, b, top_k: int, experts: ExpertSource, shared,
                 a[e] = v.ctypes.data
         return a, keep
 
-    bf16 = any(isinstance(ex, Bf16Expert) for ex in seq)
-    if bf16:
-        if not all(ex is None or isinstance(ex, Bf16Expert) for ex in seq):
-            raise TypeError("routed experts must be all int4 or all bf16")
+    kinds = {type(ex) for ex in seq if ex is not None}
+    if len(kinds) > 1:
+        raise TypeError("routed experts must all be of one kind (int4, bf16 or fp8)")
+    bf16 = Bf16Expert in kinds
+    fp8 = Fp8Expert in kinds
+    if fp8:
+        q1, k1 = arr("q1", np.uint8); s1, k2 = arr("s1", np.float32)
+        q3, k3 = arr("q3", np.uint8); s3, k4 = arr("s3", np.float32)
+        q2, k5 = arr("q2", np.uint8); s2, k6 = arr("s2", np.float32)
+        keep = (k1, k2, k3, k4, k5, k6)  # noqa: F841  (keeps arrays alive)
+        ubs = {float(ex.ub) for ex in seq if ex is not None}
+        if len(ubs) > 1:
+            raise ValueError("fp8 experts must share one activation scale bound")
+        ub = ubs.pop() if ubs else 0.0
+        f32 = np.empty(max(d, h), dtype=np.float32)
+        codes = np.empty(max(d, h), dtype=np.uint8)
+    elif bf16:
         w1, k1 = arr("w1", np.uint16); w3, k2 = arr("w3", np.uint16)
         w2, k3 = arr("w2", np.uint16)
         keep = (k1, k2, k3)  # noqa: F841  (keeps arrays alive)
@@ -150,7 +192,12 @@ def moe_forward_per_token(x, wr, b, top_k: int, experts: ExpertSource, shared,
     for t in range(T):
         tail = (_ptr(sh1), _ptr(sh3), _ptr(sh2), None if forced is None else _ptr(forced[t]),
                 _ptr(logits[t]), _ptr(ids[t]), _ptr(gates[t]), _ptr(u), _ptr(o), _ptr(y[t]))
-        if bf16:
+        if fp8:
+            rc = L.oracle_moe_token_fp8(_ptr(xf[t]), d, h, E, top_k, _ptr(wr),
+                                        None if bias is None else _ptr(bias),
+                                        q1, s1, q3, s3, q2, s2, ub, *tail[:7], _ptr(f32),
+                                        _ptr(codes), *tail[7:])
+        elif bf16:
             rc = L.oracle_moe_token_bf16(_ptr(xf[t]), d, h, E, top_k, _ptr(wr),
                                          None if bias is None else _ptr(bias), w1, w3, w2, *tail)
         else:

@@ -40,15 +40,17 @@ class Layer:
     wr_d: torch.Tensor
     b_d: Optional[torch.Tensor]
     shared_d: tuple
-    experts_d: object        # moe.Int4Experts or moe.Bf16Experts
-    routed: str = "int4"     # routed expert weights: "int4" or "bf16"
+    experts_d: object        # moe.Int4Experts, moe.Bf16Experts or moe.Fp8Experts
+    routed: str = "int4"     # routed expert weights: "int4", "bf16" or "fp8"
+    act_ub: float = 0.0      # fp8 experts: activation scale bound
 
 
 def build_layer(cfg: W.MoEConfig, dev="cuda:0", routed_draw: Optional[str] = None,
-                routed: str = "int4") -> Layer:
+                routed: str = "int4", act_ub: float = W.FP8_ACT_UB) -> Layer:
     """The layer on the GPU. Routed weights are drawn on the CPU for small
     layers and on the GPU (then quantized there) for the 5120 x 8192 ones.
-    ``routed="bf16"`` keeps the routed experts in bf16 (RNE of the same draws)."""
+    ``routed="bf16"`` keeps the routed experts in bf16 (RNE of the same draws);
+    ``routed="fp8"`` quantizes them to fp8 row-wise on the GPU (bound ``act_ub``)."""
     dev = torch.device(dev)
     if routed_draw is None:
         routed_draw = "cpu" if cfg.d * cfg.h <= 1 << 22 else str(dev)
@@ -57,6 +59,8 @@ def build_layer(cfg: W.MoEConfig, dev="cuda:0", routed_draw: Optional[str] = Non
     shared = W.gen_shared(cfg)
     if routed == "bf16":
         ex = moe.Bf16Experts.empty(cfg.E, cfg.d, cfg.h, dev)
+    elif routed == "fp8":
+        ex = moe.Fp8Experts.empty(cfg.E, cfg.d, cfg.h, dev, act_ub)
     else:
         ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev)
     for e in range(cfg.E):
@@ -70,12 +74,12 @@ def build_layer(cfg: W.MoEConfig, dev="cuda:0", routed_draw: Optional[str] = Non
     shared_d = moe.pack_shared(*(s.to(dev) for s in shared))
     torch.cuda.synchronize(dev)
     return Layer(cfg, x, wr, b, shared, routed_draw, dev, x.to(dev), wr.to(dev),
-                 None if b is None else b.to(dev), shared_d, ex, routed)
+                 None if b is None else b.to(dev), shared_d, ex, routed, float(act_ub))
 
 
 def oracle_expert(layer: Layer, e: int):
     """Expert e for the oracle from the same fp32 draw: quantized by the oracle
-    (int4 layers), or the same bf16 rounding the GPU was given (bf16 layers)."""
+    (int4 and fp8 layers), or the same bf16 rounding the GPU was given (bf16 layers)."""
     if layer.routed == "bf16":
         bits = []
         for w in ("w1", "w3", "w2"):
@@ -83,6 +87,10 @@ def oracle_expert(layer: Layer, e: int):
             bits.append(wb.view(torch.int16).numpy().view(np.uint16).copy())
             del wb
         return Bf16Expert(*bits)
+    if layer.routed == "fp8":
+        ws = [W.gen_expert_weight(layer.cfg, w, e, layer.gen_dev).cpu().numpy()
+              for w in ("w1", "w3", "w2")]
+        return native.fp8_expert(*ws, layer.act_ub)
     parts = []
     for w in ("w1", "w3", "w2"):
         wf = W.gen_expert_weight(layer.cfg, w, e, layer.gen_dev).cpu().numpy()

@@ -136,3 +136,57 @@ def test_fp8_layer_closed_form_all_ties():
     xf = x.float().numpy().astype(np.float64)
     want = 0.5 * (ex[0].ffn(xf) + ex[1].ffn(xf))
     np.testing.assert_allclose(r.y, want, rtol=0, atol=0)
+
+
+# ---- the C loop form (oracle/csrc/oracle.c) against the pinned numpy form
+
+def test_c_fp8_values_match_torch():
+    from oracle import native
+    codes, vals = _all_fp8_values()
+    ok = ~np.isnan(vals)
+    got = np.array([native.lib().oracle_fp8_value(int(c)) for c in codes[ok]])
+    np.testing.assert_array_equal(got, vals[ok])
+
+
+@pytest.mark.parametrize("ub", [None, 0.75])
+def test_c_row_quantizer_matches_numpy(ub):
+    from oracle import native
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((24, 384)) * np.exp2(rng.integers(-12, 8, (24, 1)))).astype(np.float32)
+    w[3] = 0.0                                     # all-zero row
+    w[5, :] = np.float32(2.0 ** -30)               # tiny row: scale floor 1e-12
+    codes, vals = _all_fp8_values()
+    finite = np.sort(np.unique(vals[np.isfinite(vals) & (vals >= 0)]))
+    mids = (finite[:-1] + finite[1:]) / 2            # every tie (scale 1: row maximum 448)
+    w[6, :mids.size] = mids
+    w[6, mids.size] = 448.0
+    w[7, :mids.size] = -mids
+    w[7, mids.size] = -448.0
+    qn, sn = quantize_rows(w, ub)
+    qc, sc = native.quantize_fp8_rows(w, ub)
+    np.testing.assert_array_equal(sc, sn)
+    np.testing.assert_array_equal(qc, qn)
+
+
+def test_c_fp8_layer_matches_numpy():
+    """The per-token C loop and the grouped numpy form of a small fp8 layer: the
+    fp8 sums are exact in both, so they differ only where exp() rounds apart."""
+    from oracle import native
+    rng = np.random.default_rng(11)
+    T, d, h, E, k = 9, 256, 384, 4, 2
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    wr = (rng.standard_normal((E, d)) * 0.1).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    experts = [native.fp8_expert((rng.standard_normal((h, d)) * 0.05).astype(np.float32),
+                                 (rng.standard_normal((h, d)) * 0.05).astype(np.float32),
+                                 (rng.standard_normal((d, h)) * 0.05).astype(np.float32), 2.0)
+               for _ in range(E)]
+    shared = tuple(torch.from_numpy((rng.standard_normal(s) * 0.05).astype(np.float32))
+                   .to(torch.bfloat16) for s in ((h, d), (h, d), (d, h)))
+    r_np = moe_forward(x.float().numpy(), wr, b, k, experts, shared)
+    r_c = native.moe_forward_per_token(x, wr, b, k, experts, shared)
+    np.testing.assert_array_equal(r_c.ids, r_np.ids)
+    err = np.abs(r_c.y - r_np.y).max(axis=1) / np.abs(r_np.y).max(axis=1)
+    assert err.max() < 1e-2, err.max()
+    # most rows agree to the last bit of every bf16 rounding
+    assert np.mean(err < 1e-12) >= 0.5, err
