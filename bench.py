@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--experts", default="int4", choices=["int4", "bf16", "fp8"],
                     help="routed expert weights: int4 g128 (default), bf16 (the baseline "
                          "path) or fp8 row-wise (the fp8_mixed path)")
+    ap.add_argument("--group", type=int, default=128, choices=[128, 64, 32],
+                    help="int4 experts: weights per scale (default 128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -86,8 +88,7 @@ def measured_traffic(stage: str, workload: str):
     return rec["hbm_bytes_per_launch"]
 
 
-def layer_weight_bytes(cfg, experts: str = "int4") -> int:
-    g = 128
+def layer_weight_bytes(cfg, experts: str = "int4", g: int = 128) -> int:
     if experts == "bf16":
         routed = cfg.E * 3 * cfg.h * cfg.d * 2
     elif experts == "fp8":
@@ -98,7 +99,7 @@ def layer_weight_bytes(cfg, experts: str = "int4") -> int:
     return routed + shared
 
 
-def build_layer(cfg, dev, experts: str = "int4"):
+def build_layer(cfg, dev, experts: str = "int4", group: int = 128):
     import torch
     import moe_ffn_int4_amd as moe
     import workloads as W
@@ -109,7 +110,7 @@ def build_layer(cfg, dev, experts: str = "int4"):
     elif experts == "fp8":
         ex = moe.Fp8Experts.empty(cfg.E, cfg.d, cfg.h, dev, W.FP8_ACT_UB)
     else:
-        ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev)
+        ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev, group)
     for e in range(cfg.E):
         ws = [W.gen_expert_weight(cfg, w, e, dev) for w in ("w1", "w3", "w2")]
         if experts == "bf16":
@@ -122,13 +123,12 @@ def build_layer(cfg, dev, experts: str = "int4"):
     torch.cuda.synchronize()
     return dict(cfg=cfg, x=x.to(dev), wr=wr.to(dev), b=None if b is None else b.to(dev),
                 experts=ex, shared=shared, shared_raw=shared_raw, x_cpu=x, wr_cpu=wr, b_cpu=b,
-                routed=experts)
+                routed=experts, group=group)
 
 
-def stage_units(cfg, counts, experts: str = "int4"):
+def stage_units(cfg, counts, experts: str = "int4", g: int = 128):
     """Algorithmic bytes and FLOPs of each stage for one launch, given the
-    realized per-expert pair counts of the step."""
-    g = 128
+    realized per-expert pair counts of the step (int4: g weights per scale)."""
     T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.top_k
     P = T * k
     touched = int((counts > 0).sum())
@@ -187,7 +187,8 @@ def cpu_baseline(layer, n_sample, dev, min_seconds=10.0):
             continue
         parts = []  # oracle's own quantization of the same draws
         for w in ("w1", "w3", "w2"):
-            parts.extend(native.quantize_int4(W.gen_expert_weight(cfg, w, e, dev).cpu().numpy()))
+            parts.extend(native.quantize_int4(W.gen_expert_weight(cfg, w, e, dev).cpu().numpy(),
+                                              layer["group"]))
         experts[e] = Int4Expert(*parts)
     shared = tuple(s.cpu() for s in layer["shared_raw"])
     native.lib()
@@ -195,7 +196,8 @@ def cpu_baseline(layer, n_sample, dev, min_seconds=10.0):
     reps = 0
     t0 = time.perf_counter()
     while True:
-        ref = native.moe_forward_per_token(xs, layer["wr_cpu"].numpy(), b, cfg.top_k, experts, shared)
+        ref = native.moe_forward_per_token(xs, layer["wr_cpu"].numpy(), b, cfg.top_k, experts, shared,
+                                           group_size=layer["group"])
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or reps >= 1000:
@@ -236,12 +238,13 @@ def main() -> int:
     cfg0 = W.config(ci)
     steps = args.steps if args.steps is not None else DEFAULT_STEPS[ci]
     warmup = args.warmup if args.warmup is not None else DEFAULT_WARMUP[ci]
-    nlayers = args.layers or max(2, min(8, math.ceil(4e9 / layer_weight_bytes(cfg0, args.experts))))
+    nlayers = args.layers or max(2, min(8, math.ceil(
+        4e9 / layer_weight_bytes(cfg0, args.experts, args.group))))
     print(f"[bench] config {ci} {cfg0.name}: T={cfg0.T} d={cfg0.d} E={cfg0.E} h={cfg0.h} "
           f"k={cfg0.top_k}; {nlayers} layer copies, {warmup} warmup + {steps} timed steps",
           file=sys.stderr, flush=True)
 
-    layers = [build_layer(cfg0.with_(seed=s), dev, args.experts) for s in range(nlayers)]
+    layers = [build_layer(cfg0.with_(seed=s), dev, args.experts, args.group) for s in range(nlayers)]
     ws = moe.alloc_workspace(cfg0.T, cfg0.d, cfg0.E, cfg0.h, cfg0.top_k, dev,
                              fp8=args.experts == "fp8")
     y = torch.empty(cfg0.T, cfg0.d, dtype=torch.bfloat16, device=dev)
@@ -308,7 +311,7 @@ def main() -> int:
     value = cfg0.T * steps / wall
 
     # roofline of the dominant kernel, per launch, averaged over the timed steps
-    units = [stage_units(L["cfg"], c, args.experts) for L, c in zip(layers, counts)]
+    units = [stage_units(L["cfg"], c, args.experts, args.group) for L, c in zip(layers, counts)]
     launched = {k: v for k, v in stages.items() if v[1] > 0}
     dom = max(launched, key=lambda k: launched[k][0])
     dom_ms, dom_n = launched[dom]
@@ -329,7 +332,8 @@ def main() -> int:
         peak = flops / ((flops - f8) / BF16_MFMA_PEAK_TFLOPS + f8 / FP8_MFMA_PEAK_TFLOPS)
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None}
-    roof["traffic"] = measured_traffic(dom, cfg0.name if args.experts == "int4" else None)
+    roof["traffic"] = measured_traffic(
+        dom, cfg0.name if (args.experts == "int4" and args.group == 128) else None)
     if roof["traffic"] is not None:
         roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
     roof["kernel"] = dom
@@ -365,7 +369,7 @@ def main() -> int:
         "dtype": "fp8+bf16" if args.experts == "fp8" else "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg0.name}: T={cfg0.T} d={cfg0.d} E={cfg0.E}+1 shared "
                                f"h={cfg0.h} top_k={cfg0.top_k}, "
-                               + {"int4": "int4 g128", "bf16": "bf16",
+                               + {"int4": f"int4 g{args.group}", "bf16": "bf16",
                                   "fp8": f"fp8 row-wise (act ub {W.FP8_ACT_UB:g})"}[args.experts]
                                + " routed / bf16 shared",
                    "T": cfg0.T, "d": cfg0.d, "E": cfg0.E, "h": cfg0.h, "top_k": cfg0.top_k,

@@ -10,8 +10,10 @@
  * Expert FFN (docs.ifdog.com page "Llama 开源模型系列", section
  * "SwiGLU：门控激活的数学"): (Swish(x W1^T) * (x W3^T)) W2^T with
  * Swish(z) = z * sigmoid(z). Routed-expert weights are int4 in groups of 128
- * (same discosf.com page, section "FP8 / Int4 混合量化"); activations and the
- * shared expert stay bf16 (lshu.cn page, section "量化环节").
+ * (same discosf.com page, section "FP8 / Int4 混合量化"), or of 64 or 32: the
+ * smaller group sizes the lshu.cn page expects next (section "维护状态");
+ * activations and the shared expert stay bf16 (lshu.cn page, section
+ * "量化环节").
  *
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers on the current HIP device, owned
@@ -60,7 +62,7 @@ enum moe_path {
 };
 
 /* Limits checked by validation. */
-#define MOE_GROUP_SIZE 128     /* the only supported quantization group */
+#define MOE_GROUP_SIZE 128     /* the default quantization group; 64 and 32 are also supported */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOP_K 16
 
@@ -83,11 +85,11 @@ int moe_device_check(void);
  * row: scale = max(max|w|, 1e-6f) / 8, code = clamp(round_half_even(w / scale),
  * -8, 7), in fp32 with a correctly rounded division.
  *
- *   w       fp32 [rows, K], K % group_size == 0, 16-byte aligned
+ *   w       fp32 [rows, K], K % 128 == 0, 16-byte aligned
  *   q       out, uint8 [rows, K/2]: byte j of a row holds code 2j in its low
  *           nibble and code 2j+1 in its high nibble, 4-bit two's complement
  *   scales  out, fp32 [rows, K/group_size]
- *   group_size  must be MOE_GROUP_SIZE
+ *   group_size  128 (MOE_GROUP_SIZE), 64 or 32
  */
 int moe_quantize_int4(const float *w, int64_t rows, int64_t K, int32_t group_size,
                       uint8_t *q, float *scales, void *stream);
@@ -97,10 +99,11 @@ int moe_quantize_int4(const float *w, int64_t rows, int64_t K, int32_t group_siz
  * (MI355X-specific storage; codes and scales are bit-identical to
  * moe_quantize_int4, only their order in memory differs). rows % 16 == 0.
  * Tile (rb, g) covers rows 16*rb .. 16*rb+15 and reduction columns
- * 128*g .. 128*g+127; tiles are stored rb-major, t = rb * (K/128) + g:
+ * 128*g .. 128*g+127; tiles are stored rb-major, t = rb * (K/128) + g. With
+ * S = 128 / group_size scales per tile row:
  *   q       byte  t*1024 + (row % 16)*64 + (k % 128)/2   (low nibble = even k)
- *   scales  float t*16 + (row % 16)
- * A wavefront reads one 1 KB tile (and its 64 B of scales) per access.
+ *   scales  float (t*16 + row % 16)*S + (k % 128)/group_size
+ * A wavefront reads one 1 KB tile (and its 64*S B of scales) per access.
  */
 int moe_quantize_int4_tiled(const float *w, int64_t rows, int64_t K, int32_t group_size,
                             uint8_t *q, float *scales, void *stream);
@@ -122,13 +125,14 @@ typedef struct moe_dims {
     int64_t E;      /* routed experts, 1..MOE_MAX_EXPERTS */
     int64_t h;      /* expert hidden dim, multiple of 128 */
     int32_t top_k;  /* 1..min(E, MOE_MAX_TOP_K) */
-    int32_t group_size; /* must be MOE_GROUP_SIZE */
+    int32_t group_size; /* int4 quantization group: 128, 64 or 32 */
 } moe_dims;
 
-/* Routed experts, each matrix written by moe_quantize_int4_tiled, experts
- * stacked (expert e's matrix starts at e times the matrix size):
- *   w1q, w3q [E] x tiled [h, d]: E*h*d/2 bytes   w1s, w3s: E*h*d/128 fp32
- *   w2q      [E] x tiled [d, h]: E*d*h/2 bytes   w2s:      E*d*h/128 fp32 */
+/* Routed experts, each matrix written by moe_quantize_int4_tiled with
+ * dims->group_size (g), experts stacked (expert e's matrix starts at e times
+ * the matrix size):
+ *   w1q, w3q [E] x tiled [h, d]: E*h*d/2 bytes   w1s, w3s: E*h*d/g fp32
+ *   w2q      [E] x tiled [d, h]: E*d*h/2 bytes   w2s:      E*d*h/g fp32 */
 typedef struct moe_experts_int4 {
     const uint8_t *w1q, *w3q, *w2q;
     const float *w1s, *w3s, *w2s;

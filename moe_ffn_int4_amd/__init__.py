@@ -27,7 +27,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_int4.so")
-GROUP = 128
+GROUP = 128                 # default int4 quantization group
+GROUPS = (128, 64, 32)      # supported int4 groups (weights per scale)
+TILE = 128                  # columns of a weight tile
 PATHS = {"auto": 0, "prefill": 1, "decode": 2, "hybrid": 3}
 
 MOE_OK = 0
@@ -153,19 +155,21 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _dims(T, d, E, h, top_k) -> _Dims:
-    return _Dims(int(T), int(d), int(E), int(h), int(top_k), GROUP)
+def _dims(T, d, E, h, top_k, group: int = GROUP) -> _Dims:
+    return _Dims(int(T), int(d), int(E), int(h), int(top_k), int(group))
 
 
 # --------------------------------------------------------------- quantizer
 
 def quantize_int4(w: torch.Tensor, q: Optional[torch.Tensor] = None,
-                  scales: Optional[torch.Tensor] = None, tiled: bool = False):
-    """Int4 group quantizer: fp32 [rows, K] -> (uint8 [rows, K/2], fp32 [rows, K/128]).
+                  scales: Optional[torch.Tensor] = None, tiled: bool = False,
+                  group: int = GROUP):
+    """Int4 group quantizer: fp32 [rows, K] -> (uint8 [rows, K/2], fp32 [rows, K/group]).
 
     ``w`` may have leading batch dims; they are flattened into rows. With
     ``tiled`` the outputs hold the same codes and scales in the 16-row tile
-    order the forward pass reads (rows must be a multiple of 16).
+    order the forward pass reads (rows must be a multiple of 16). ``group``:
+    128, 64 or 32 weights per scale (K a multiple of 128).
     """
     _need(w, "w", torch.float32)
     K = w.shape[-1]
@@ -173,13 +177,13 @@ def quantize_int4(w: torch.Tensor, q: Optional[torch.Tensor] = None,
     if q is None:
         q = torch.empty(w.shape[:-1] + (K // 2,), dtype=torch.uint8, device=w.device)
     if scales is None:
-        scales = torch.empty(w.shape[:-1] + (K // GROUP,), dtype=torch.float32, device=w.device)
+        scales = torch.empty(w.shape[:-1] + (K // group,), dtype=torch.float32, device=w.device)
     _need(q, "q", torch.uint8)
     _need(scales, "scales", torch.float32)
-    if q.numel() != rows * (K // 2) or scales.numel() != rows * (K // GROUP):
+    if q.numel() != rows * (K // 2) or scales.numel() != rows * (K // group):
         raise ValueError("q / scales have the wrong number of elements")
     fn = lib().moe_quantize_int4_tiled if tiled else lib().moe_quantize_int4
-    _check(fn(_ptr(w), rows, K, GROUP, _ptr(q), _ptr(scales), _stream(w.device)))
+    _check(fn(_ptr(w), rows, K, int(group), _ptr(q), _ptr(scales), _stream(w.device)))
     return q, scales
 
 
@@ -241,9 +245,9 @@ class Int4Experts:
     w1q: torch.Tensor  # uint8 [E, h, d/2]
     w3q: torch.Tensor  # uint8 [E, h, d/2]
     w2q: torch.Tensor  # uint8 [E, d, h/2]
-    w1s: torch.Tensor  # fp32  [E, h, d/128]
-    w3s: torch.Tensor  # fp32  [E, h, d/128]
-    w2s: torch.Tensor  # fp32  [E, d, h/128]
+    w1s: torch.Tensor  # fp32  [E, h, d/group]
+    w3s: torch.Tensor  # fp32  [E, h, d/group]
+    w2s: torch.Tensor  # fp32  [E, d, h/group]
 
     @property
     def E(self) -> int:
@@ -257,28 +261,40 @@ class Int4Experts:
     def d(self) -> int:
         return self.w2q.shape[1]
 
+    @property
+    def group(self) -> int:
+        """Weights per scale (128, 64 or 32)."""
+        return self.d // self.w1s.shape[2]
+
     @staticmethod
-    def empty(E: int, d: int, h: int, device) -> "Int4Experts":
+    def empty(E: int, d: int, h: int, device, group: int = GROUP) -> "Int4Experts":
+        if group not in GROUPS:
+            raise ValueError(f"group {group} unsupported {GROUPS}")
         u8, f32 = torch.uint8, torch.float32
         return Int4Experts(
             torch.empty(E, h, d // 2, dtype=u8, device=device),
             torch.empty(E, h, d // 2, dtype=u8, device=device),
             torch.empty(E, d, h // 2, dtype=u8, device=device),
-            torch.empty(E, h, d // GROUP, dtype=f32, device=device),
-            torch.empty(E, h, d // GROUP, dtype=f32, device=device),
-            torch.empty(E, d, h // GROUP, dtype=f32, device=device))
+            torch.empty(E, h, d // group, dtype=f32, device=device),
+            torch.empty(E, h, d // group, dtype=f32, device=device),
+            torch.empty(E, d, h // group, dtype=f32, device=device))
 
     def quantize_expert(self, e: int, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor):
         """Quantize one expert's fp32 weights (on the GPU) into slot ``e`` (tiled)."""
-        quantize_int4(w1, self.w1q[e], self.w1s[e], tiled=True)
-        quantize_int4(w3, self.w3q[e], self.w3s[e], tiled=True)
-        quantize_int4(w2, self.w2q[e], self.w2s[e], tiled=True)
+        g = self.group
+        quantize_int4(w1, self.w1q[e], self.w1s[e], tiled=True, group=g)
+        quantize_int4(w3, self.w3q[e], self.w3s[e], tiled=True, group=g)
+        quantize_int4(w2, self.w2q[e], self.w2s[e], tiled=True, group=g)
 
     def _struct(self) -> _Experts:
         for name in ("w1q", "w3q", "w2q"):
             _need(getattr(self, name), name, torch.uint8)
         for name in ("w1s", "w3s", "w2s"):
             _need(getattr(self, name), name, torch.float32)
+        g = self.group
+        if (g not in GROUPS or self.w1s.shape[2] * g != self.d or self.w3s.shape != self.w1s.shape
+                or self.w2s.shape[2] * g != self.h):
+            raise ValueError("int4 scales do not match one of the supported groups")
         return _Experts(*(getattr(self, n).data_ptr() for n in
                           ("w1q", "w3q", "w2q", "w1s", "w3s", "w2s")))
 
@@ -423,7 +439,7 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Te
     fp8 = isinstance(experts, Fp8Experts)
     if workspace is None:
         workspace = alloc_workspace(T, d, E, h, top_k, x.device, fp8)
-    dims = _dims(T, d, E, h, top_k)
+    dims = _dims(T, d, E, h, top_k, experts.group if isinstance(experts, Int4Experts) else GROUP)
     ex = experts._struct()
     sh = _Shared(s1.data_ptr(), s3.data_ptr(), s2.data_ptr())
     if fp8:
@@ -474,17 +490,18 @@ def route(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tens
 
 def untile_int4(q: torch.Tensor, rows: int, K: int) -> torch.Tensor:
     """Tiled int4 bytes of one [rows, K] matrix -> row-major bytes [rows, K/2]."""
-    return q.reshape(rows // 16, K // GROUP, 16, GROUP // 2).permute(0, 2, 1, 3).reshape(rows, K // 2)
+    return q.reshape(rows // 16, K // TILE, 16, TILE // 2).permute(0, 2, 1, 3).reshape(rows, K // 2)
 
 
-def untile_scales(s: torch.Tensor, rows: int, K: int) -> torch.Tensor:
-    """Tiled scales of one [rows, K] matrix -> row-major [rows, K/128]."""
-    return s.reshape(rows // 16, K // GROUP, 16).permute(0, 2, 1).reshape(rows, K // GROUP)
+def untile_scales(s: torch.Tensor, rows: int, K: int, group: int = GROUP) -> torch.Tensor:
+    """Tiled scales of one [rows, K] matrix -> row-major [rows, K/group]."""
+    S = TILE // group
+    return s.reshape(rows // 16, K // TILE, 16, S).permute(0, 2, 1, 3).reshape(rows, K // group)
 
 
 def untile_bf16(t: torch.Tensor, rows: int, K: int) -> torch.Tensor:
     """Tiled bf16 [rows, K] (pack_bf16_tiled order) -> row-major [rows, K]."""
-    return t.reshape(rows // 16, K // GROUP, 4, 16, 32).permute(0, 3, 1, 2, 4).reshape(rows, K)
+    return t.reshape(rows // 16, K // TILE, 4, 16, 32).permute(0, 3, 1, 2, 4).reshape(rows, K)
 
 
 def unpack_int4(q: torch.Tensor) -> torch.Tensor:

@@ -106,11 +106,12 @@ constexpr int64_t kHybridAvgPairs = 256;
 // MOE_PATH_HYBRID: routed experts with at most this many pairs stream
 constexpr int kHybridRows = 32;
 
+bool group_ok(int32_t g) { return g == 128 || g == 64 || g == 32; }
+
 int check_dims(const moe_dims* d) {
     if (!d) return fail(MOE_ERR_INVALID_ARG, "dims is NULL");
-    if (d->group_size != MOE_GROUP_SIZE)
-        return fail(MOE_ERR_INVALID_ARG, "group_size %d unsupported (only %d)", d->group_size,
-                    MOE_GROUP_SIZE);
+    if (!group_ok(d->group_size))
+        return fail(MOE_ERR_INVALID_ARG, "group_size %d unsupported (128, 64 or 32)", d->group_size);
     if (d->T < 1) return fail(MOE_ERR_INVALID_ARG, "T = %lld must be >= 1", (long long)d->T);
     if (d->d < 128 || d->d % 128)
         return fail(MOE_ERR_INVALID_ARG, "d = %lld must be a positive multiple of 128", (long long)d->d);
@@ -319,13 +320,11 @@ int moe_device_check(void) { return device_ok(); }
 static int quantize(const float* w, int64_t rows, int64_t K, int32_t group_size, uint8_t* q,
                     float* scales, bool tiled, void* stream) {
     g_last_error.clear();
-    if (group_size != MOE_GROUP_SIZE)
-        return fail(MOE_ERR_INVALID_ARG, "group_size %d unsupported (only %d)", group_size,
-                    MOE_GROUP_SIZE);
+    if (!group_ok(group_size))
+        return fail(MOE_ERR_INVALID_ARG, "group_size %d unsupported (128, 64 or 32)", group_size);
     if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows = %lld is negative", (long long)rows);
-    if (K < group_size || K % group_size)
-        return fail(MOE_ERR_INVALID_ARG, "K = %lld must be a positive multiple of %d", (long long)K,
-                    group_size);
+    if (K < 128 || K % 128)
+        return fail(MOE_ERR_INVALID_ARG, "K = %lld must be a positive multiple of 128", (long long)K);
     if (tiled && rows % 16)
         return fail(MOE_ERR_INVALID_ARG, "rows = %lld must be a multiple of 16 for the tiled layout",
                     (long long)rows);
@@ -334,7 +333,8 @@ static int quantize(const float* w, int64_t rows, int64_t K, int32_t group_size,
     CHECK(check_ptr(q, "q", tiled ? 16 : 2));
     CHECK(check_ptr(scales, "scales", 4));
     CHECK(device_ok());
-    HIP_CHECK(moe::launch_quantize_int4(w, rows, K, q, scales, tiled, static_cast<hipStream_t>(stream)),
+    HIP_CHECK(moe::launch_quantize_int4(w, rows, K, group_size, q, scales, tiled,
+                                        static_cast<hipStream_t>(stream)),
               "quantize launch");
     return MOE_OK;
 }
@@ -537,6 +537,7 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         a.a_perm = x_perm;
         a.K = d.d;
         a.N = d.h;
+        a.spt = moe::kGroup / d.group_size;
         if (ex4) {
             a.wq0 = ex4->w1q;
             a.ws0 = ex4->w1s;
@@ -572,6 +573,7 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         a.a_perm = H;  // routed rows of H were written interleaved by the streaming up projection
         a.K = d.h;
         a.N = d.d;
+        a.spt = moe::kGroup / d.group_size;
         if (ex4) {
             a.wq0 = ex4->w2q;
             a.ws0 = ex4->w2s;
@@ -614,6 +616,7 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         g.a = x;
         g.K = d.d;
         g.N = d.h;
+        g.spt = moe::kGroup / d.group_size;
         if (ex4) {
             g.wq0 = ex4->w1q;
             g.ws0 = ex4->w1s;

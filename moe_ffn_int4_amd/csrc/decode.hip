@@ -31,6 +31,15 @@
 // 8 codes, so the A rows of routed experts are stored with their 8-element
 // blocks in that order: x by the router kernel (x_perm), H by this kernel's
 // up-projection epilogue. bf16 weights (the shared expert) use natural order.
+// Groups of 64 or 32 weights (S = 2 or 4 scales per 128-column tile row): one
+// MFMA step must then stay inside one group, but a lane's 16 bytes hold 32
+// consecutive codes, and the four kq lanes of a step would span four groups.
+// A 4 x 4 transpose of the lanes' words across the four 16-lane rows
+// (v_permlane32_swap, then v_permlane16_swap) gives lane kq the words
+// kq, 4 + kq, 8 + kq, 12 + kq of its feature's row instead: step i then covers
+// columns 32 i .. 32 i + 31 of the tile (one group of 32, or half of one of 64),
+// the A row is read at 32 i + 8 kq, and each group's accumulator takes its
+// own scale.
 #include "common.h"
 #include "kernels.h"
 
@@ -63,39 +72,117 @@ __device__ __forceinline__ uint4 offset_bf16(uint32_t w) {
     return r;
 }
 
+// S scales per 128-column tile row of an int4 weight: 128 / group
+template <int S>
 struct RoutedSlot {
     uint4 w0, w1;
-    float s0, s1;
+    float s0[S], s1[S];
     uint4 a[4];
 };
 
+template <int S>
 struct WeightSlot {
     uint4 w0, w1;
-    float s0, s1;
+    float s0[S], s1[S];
 };
+
+// this lane's S scales of tile g: one float, or an aligned float2 / float4
+template <int S>
+__device__ __forceinline__ void load_scales(float (&d)[S], const float* s, int g) {
+    if constexpr (S == 1) {
+        d[0] = ld_stream_f(s + g * 16);
+    } else {
+        typedef float fv __attribute__((ext_vector_type(S)));
+        const fv v = __builtin_nontemporal_load(reinterpret_cast<const fv*>(s + g * 16 * S));
+#pragma unroll
+        for (int j = 0; j < S; ++j) d[j] = v[j];
+    }
+}
+
+// word j of lane (n, row r) -> word r of lane (n, row j), rows of 16 lanes
+__device__ __forceinline__ uint4 transpose_rows(uint4 v) {
+    // rows 0-1 x words 2-3 <-> rows 2-3 x words 0-1
+    const auto p = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+    const auto q = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+    // odd rows x even words <-> even rows x odd words
+    const auto r = __builtin_amdgcn_permlane16_swap(p[0], q[0], false, false);
+    const auto t = __builtin_amdgcn_permlane16_swap(p[1], q[1], false, false);
+    return make_uint4(r[0], r[1], t[0], t[1]);
+}
 
 struct SharedSlot {
     uint4 b0[4], b1[4];
     uint4 a[4];
 };
 
-// group g of this lane's piece of a 16-row int4 tile (1 KB per tile) and its scale
-template <bool UP>
-__device__ __forceinline__ void load_routed(RoutedSlot& sl, const uint8_t* q0, const uint8_t* q1,
+// A column step of MFMA step i: this lane's 8 columns sit at 8 i (S = 1: the
+// lane's 32 columns are contiguous) or at 32 i (S > 1: after the transpose)
+template <int S>
+constexpr int a_step() { return S == 1 ? 8 : 32; }
+
+// tile g of this lane's piece of a 16-row int4 tile (1 KB per tile) and its scales
+template <bool UP, int S>
+__device__ __forceinline__ void load_routed(RoutedSlot<S>& sl, const uint8_t* q0, const uint8_t* q1,
                                             const float* s0, const float* s1, const uint16_t* arow,
                                             int g) {
     sl.w0 = ld_stream(q0 + g * 1024);
-    sl.s0 = ld_stream_f(s0 + g * 16);
+    load_scales<S>(sl.s0, s0, g);
     if (UP) {
         sl.w1 = ld_stream(q1 + g * 1024);
-        sl.s1 = ld_stream_f(s1 + g * 16);
+        load_scales<S>(sl.s1, s1, g);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sl.a[i] = *reinterpret_cast<const uint4*>(arow + g * kGroup + i * 8);
+    for (int i = 0; i < 4; ++i)
+        sl.a[i] = *reinterpret_cast<const uint4*>(arow + g * kGroup + i * a_step<S>());
 }
 
-template <bool UP>
-__device__ __forceinline__ void compute_routed(const RoutedSlot& sl, f32x4& acc0, f32x4& acc1) {
+// S > 1: group j of the tile covers MFMA steps 4j/S .. 4(j+1)/S - 1 and has
+// its own -136 correction, accumulator and scale
+template <bool UP, int S>
+__device__ __forceinline__ void compute_groups(const RoutedSlot<S>& sl, f32x4& acc0, f32x4& acc1) {
+    constexpr int SPG = 4 / S;  // MFMA steps per group
+    const bf16x8 neg136 = as_bf16x8(make_uint4(kNeg136, kNeg136, kNeg136, kNeg136));
+    const uint4 t0 = transpose_rows(sl.w0);
+    const uint32_t w0[4] = {t0.x, t0.y, t0.z, t0.w};
+    uint32_t w1[4] = {0u, 0u, 0u, 0u};
+    if (UP) {
+        const uint4 t1 = transpose_rows(sl.w1);
+        w1[0] = t1.x;
+        w1[1] = t1.y;
+        w1[2] = t1.z;
+        w1[3] = t1.w;
+    }
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        f32x4 corr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = j * SPG; i < (j + 1) * SPG; ++i)
+            corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sl.a[i]), neg136, corr, 0, 0, 0);
+        f32x4 g0 = corr;
+#pragma unroll
+        for (int i = j * SPG; i < (j + 1) * SPG; ++i)
+            g0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sl.a[i]),
+                                                         as_bf16x8(offset_bf16(w0[i])), g0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc0[r] = fmaf(sl.s0[j], g0[r], acc0[r]);
+        if (UP) {
+            f32x4 g1 = corr;
+#pragma unroll
+            for (int i = j * SPG; i < (j + 1) * SPG; ++i)
+                g1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sl.a[i]),
+                                                             as_bf16x8(offset_bf16(w1[i])), g1, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc1[r] = fmaf(sl.s1[j], g1[r], acc1[r]);
+        }
+    }
+}
+
+template <bool UP, int S>
+__device__ __forceinline__ void compute_routed(const RoutedSlot<S>& sl, f32x4& acc0, f32x4& acc1) {
+    if constexpr (S > 1) {
+        compute_groups<UP, S>(sl, acc0, acc1);
+        return;
+    }
     const bf16x8 neg136 = as_bf16x8(make_uint4(kNeg136, kNeg136, kNeg136, kNeg136));
     f32x4 corr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -108,7 +195,7 @@ __device__ __forceinline__ void compute_routed(const RoutedSlot& sl, f32x4& acc0
         g0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sl.a[i]), as_bf16x8(offset_bf16(w0[i])),
                                                      g0, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc0[r] = fmaf(sl.s0, g0[r], acc0[r]);
+    for (int r = 0; r < 4; ++r) acc0[r] = fmaf(sl.s0[0], g0[r], acc0[r]);
     if (UP) {
         const uint32_t w1[4] = {sl.w1.x, sl.w1.y, sl.w1.z, sl.w1.w};
         f32x4 g1 = corr;
@@ -117,35 +204,39 @@ __device__ __forceinline__ void compute_routed(const RoutedSlot& sl, f32x4& acc0
             g1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sl.a[i]),
                                                          as_bf16x8(offset_bf16(w1[i])), g1, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc1[r] = fmaf(sl.s1, g1[r], acc1[r]);
+        for (int r = 0; r < 4; ++r) acc1[r] = fmaf(sl.s1[0], g1[r], acc1[r]);
     }
 }
 
 // group g of a step-major bf16 tile (4 steps x 16 rows x 32 columns, 4 KB):
 // step i is 1 KB, this lane's piece is row l16, columns 8*kq .. 8*kq+7
-template <bool UP>
-__device__ __forceinline__ void load_weights(WeightSlot& sl, const uint8_t* q0, const uint8_t* q1,
+template <bool UP, int S>
+__device__ __forceinline__ void load_weights(WeightSlot<S>& sl, const uint8_t* q0, const uint8_t* q1,
                                              const float* s0, const float* s1, int g) {
     sl.w0 = ld_stream(q0 + g * 1024);
-    sl.s0 = ld_stream_f(s0 + g * 16);
+    load_scales<S>(sl.s0, s0, g);
     if (UP) {
         sl.w1 = ld_stream(q1 + g * 1024);
-        sl.s1 = ld_stream_f(s1 + g * 16);
+        load_scales<S>(sl.s1, s1, g);
     }
 }
 
-// one int4 group with A fragments from LDS (row `lrow` of the staged chunk)
-template <bool UP>
-__device__ __forceinline__ void compute_lds(const WeightSlot& w, const uint16_t* lrow, int g,
+// one int4 tile with A fragments from LDS (row `lrow` of the staged chunk)
+template <bool UP, int S>
+__device__ __forceinline__ void compute_lds(const WeightSlot<S>& w, const uint16_t* lrow, int g,
                                             f32x4& acc0, f32x4& acc1) {
-    RoutedSlot sl;
+    RoutedSlot<S> sl;
     sl.w0 = w.w0;
     sl.w1 = w.w1;
-    sl.s0 = w.s0;
-    sl.s1 = w.s1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sl.a[i] = *reinterpret_cast<const uint4*>(lrow + g * kGroup + i * 8);
-    compute_routed<UP>(sl, acc0, acc1);
+    for (int j = 0; j < S; ++j) {
+        sl.s0[j] = w.s0[j];
+        sl.s1[j] = w.s1[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        sl.a[i] = *reinterpret_cast<const uint4*>(lrow + g * kGroup + i * a_step<S>());
+    compute_routed<UP, S>(sl, acc0, acc1);
 }
 
 template <bool UP>
@@ -216,8 +307,8 @@ __device__ __forceinline__ void compute_fp8(const Fp8Slot& sl, f32x4& acc0, f32x
 // DR / DS: groups kept in flight ahead of the one being computed, for int4
 // (routed) and bf16 (shared) weights
 // F8: the routed experts are fp8 (a separate instantiation, so the int4 one
-// keeps its register budget)
-template <bool UP, int DR, int DS, int DL, bool F8>
+// keeps its register budget); S: int4 scales per 128-column tile row
+template <bool UP, int DR, int DS, int DL, bool F8, int S>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     // routed chunks of at most a.lds_rows rows keep their A rows in LDS
     extern __shared__ __attribute__((aligned(16))) uint16_t a_lds[];
@@ -258,7 +349,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     int64_t src;
     if (UP) src = routed ? a.perm[row0 + m] / a.top_k : row0 + m - a.P;
     else src = row0 + m;
-    const uint16_t* arow = (int4 ? a.a_perm : a.a) + src * K + (int4 ? kq * 32 : kq * 8);
+    const uint16_t* arow = (int4 ? a.a_perm : a.a) + src * K + ((int4 && S == 1) ? kq * 32 : kq * 8);
 
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     if (fp8) {
@@ -311,11 +402,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         const int64_t rb = static_cast<int64_t>(group) * (N / 16) + (n >> 4);
         const uint8_t* q0 = a.wq0 + rb * ng * 1024 + l16 * 64 + kq * 16;
         const uint8_t* q1 = UP ? a.wq1 + rb * ng * 1024 + l16 * 64 + kq * 16 : nullptr;
-        const float* s0 = a.ws0 + rb * ng * 16 + l16;
-        const float* s1 = UP ? a.ws1 + rb * ng * 16 + l16 : nullptr;
-        WeightSlot sl[U];
+        const float* s0 = a.ws0 + (rb * ng * 16 + l16) * S;
+        const float* s1 = UP ? a.ws1 + (rb * ng * 16 + l16) * S : nullptr;
+        WeightSlot<S> sl[U];
 #pragma unroll
-        for (int p = 0; p < D; ++p) load_weights<UP>(sl[p], q0, q1, s0, s1, min(p, ng - 1));
+        for (int p = 0; p < D; ++p) load_weights<UP, S>(sl[p], q0, q1, s0, s1, min(p, ng - 1));
         const int64_t pitch = K + 8;  // 16-byte pad between rows
         for (int64_t idx = tid; idx < static_cast<int64_t>(nrows) * (K / 8); idx += NT) {
             const int r = static_cast<int>(idx / (K / 8));
@@ -325,18 +416,18 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
                 *reinterpret_cast<const uint4*>(a.a_perm + srow * K + col);
         }
         __syncthreads();
-        const uint16_t* lrow = a_lds + m * pitch + kq * 32;
+        const uint16_t* lrow = a_lds + m * pitch + (S == 1 ? kq * 32 : kq * 8);
         const int full = ng - ng % U;
         for (int g0 = 0; g0 < full; g0 += U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                load_weights<UP>(sl[(u + D) % U], q0, q1, s0, s1, min(g0 + u + D, ng - 1));
-                compute_lds<UP>(sl[u], lrow, g0 + u, acc0, acc1);
+                load_weights<UP, S>(sl[(u + D) % U], q0, q1, s0, s1, min(g0 + u + D, ng - 1));
+                compute_lds<UP, S>(sl[u], lrow, g0 + u, acc0, acc1);
             }
         }
 #pragma unroll
         for (int u = 0; u < D; ++u)
-            if (u < ng - full) compute_lds<UP>(sl[u], lrow, full + u, acc0, acc1);
+            if (u < ng - full) compute_lds<UP, S>(sl[u], lrow, full + u, acc0, acc1);
     } else if (int4) {
         constexpr int D = DR;
         constexpr int U = D + 1;
@@ -344,26 +435,26 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         const int64_t rb = static_cast<int64_t>(group) * (N / 16) + (n >> 4);
         const uint8_t* q0 = a.wq0 + rb * ng * 1024 + l16 * 64 + kq * 16;
         const uint8_t* q1 = UP ? a.wq1 + rb * ng * 1024 + l16 * 64 + kq * 16 : nullptr;
-        const float* s0 = a.ws0 + rb * ng * 16 + l16;
-        const float* s1 = UP ? a.ws1 + rb * ng * 16 + l16 : nullptr;
+        const float* s0 = a.ws0 + (rb * ng * 16 + l16) * S;
+        const float* s1 = UP ? a.ws1 + (rb * ng * 16 + l16) * S : nullptr;
         // Ring of U slots, group g in slot g % U. Loads past the last group re-read
         // it (cache hits), so every loop iteration issues the same loads and the
         // compiler can wait on exact load counts; full rounds of U groups run
         // without guards, the last ng % U groups are already in their slots.
-        RoutedSlot sl[U];
+        RoutedSlot<S> sl[U];
 #pragma unroll
-        for (int p = 0; p < D; ++p) load_routed<UP>(sl[p], q0, q1, s0, s1, arow, min(p, ng - 1));
+        for (int p = 0; p < D; ++p) load_routed<UP, S>(sl[p], q0, q1, s0, s1, arow, min(p, ng - 1));
         const int full = ng - ng % U;
         for (int g0 = 0; g0 < full; g0 += U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                load_routed<UP>(sl[(u + D) % U], q0, q1, s0, s1, arow, min(g0 + u + D, ng - 1));
-                compute_routed<UP>(sl[u], acc0, acc1);
+                load_routed<UP, S>(sl[(u + D) % U], q0, q1, s0, s1, arow, min(g0 + u + D, ng - 1));
+                compute_routed<UP, S>(sl[u], acc0, acc1);
             }
         }
 #pragma unroll
         for (int u = 0; u < D; ++u)
-            if (u < ng - full) compute_routed<UP>(sl[u], acc0, acc1);
+            if (u < ng - full) compute_routed<UP, S>(sl[u], acc0, acc1);
     } else {
         // this wave's quarter of the groups: gb .. gb + cnt - 1 (cnt may be 0)
         constexpr int D = DS;
@@ -440,7 +531,8 @@ static int lds_rows(int64_t K) {
 // grid: N / 64 feature ranges x (chunks + 3 extra rows per shared-expert chunk);
 // max_chunks bounds the chunk list, shared_chunks is the number of shared-expert
 // chunks at its head (0 when the shared expert runs on the GEMMs)
-template <bool UP, int DR, int DS, int DL>
+// F8 / S pick the kernel instantiation (fp8 experts, int4 scales per tile row)
+template <bool UP, int DR, int DS, int DL, bool F8, int S>
 static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, int shared_chunks,
                                 hipStream_t stream) {
     DecodeArgs a = args;
@@ -449,19 +541,29 @@ static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, int shar
     size_t lds = a.lds_rows > 0 ? static_cast<size_t>(a.lds_rows) * (a.K + 8) * 2 : 0;
     lds = lds > kReduceLdsBytes ? lds : kReduceLdsBytes;
     dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks + 3 * shared_chunks));
-    if (a.wf0) hipLaunchKernelGGL((decode_kernel<UP, DR, DS, DL, true>), grid, dim3(NT), lds, stream, a);
-    else hipLaunchKernelGGL((decode_kernel<UP, DR, DS, DL, false>), grid, dim3(NT), lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<UP, DR, DS, DL, F8, S>), grid, dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
 
+// ring depths (tiles in flight): DR routed chunks reading A from global
+// memory, DS bf16 chunks, DL routed chunks with A staged in LDS; smaller
+// int4 groups hold more scales per slot and take shallower rings (measured on
+// the Scout decode layer: groups of 64 up 119 -> 108 us, groups of 32 up
+// 126 -> 118 us and down 86 -> 79 us against the depths of groups of 128)
 hipError_t launch_decode_up(const DecodeArgs& args, int max_chunks, int shared_chunks,
                             hipStream_t stream) {
-    return launch_decode<true, 3, 1, 7>(args, max_chunks, shared_chunks, stream);
+    if (args.wf0) return launch_decode<true, 3, 1, 7, true, 1>(args, max_chunks, shared_chunks, stream);
+    if (args.spt == 2) return launch_decode<true, 3, 1, 5, false, 2>(args, max_chunks, shared_chunks, stream);
+    if (args.spt == 4) return launch_decode<true, 2, 1, 4, false, 4>(args, max_chunks, shared_chunks, stream);
+    return launch_decode<true, 3, 1, 7, false, 1>(args, max_chunks, shared_chunks, stream);
 }
 
 hipError_t launch_decode_down(const DecodeArgs& args, int max_chunks, int shared_chunks,
                               hipStream_t stream) {
-    return launch_decode<false, 3, 2, 7>(args, max_chunks, shared_chunks, stream);
+    if (args.wf0) return launch_decode<false, 3, 2, 7, true, 1>(args, max_chunks, shared_chunks, stream);
+    if (args.spt == 2) return launch_decode<false, 3, 2, 7, false, 2>(args, max_chunks, shared_chunks, stream);
+    if (args.spt == 4) return launch_decode<false, 2, 2, 5, false, 4>(args, max_chunks, shared_chunks, stream);
+    return launch_decode<false, 3, 2, 7, false, 1>(args, max_chunks, shared_chunks, stream);
 }
 
 }  // namespace moe

@@ -5,7 +5,8 @@
 // shared expert runs on every token. The expert FFN is
 // (Swish(x W1^T) * (x W3^T)) W2^T (docs.ifdog.com page "Llama 开源模型系列",
 // section "SwiGLU：门控激活的数学"). Routed weights are int4 with one fp32
-// scale per 128 weights of a row and dequantize symmetrically as code * scale
+// scale per group of 128 (or 64, 32) weights of a row and dequantize
+// symmetrically as code * scale
 // (lshu.cn page, section "量化环节": zero-points are all zero).
 //
 // One launch covers all groups: routed experts 0..E-1 (int4 weights, rows =
@@ -24,7 +25,7 @@
 //   down: O[slot, m]  = (H W2^T)[m]                    (fp32 out)
 //
 // Block tile 128 rows x 256 B-rows, reduction step 32 (a quarter of a
-// quantization group); 256 threads = 4 waves in a 2 x 2 grid, each wave 64 x
+// 128-column weight tile, inside one quantization group); 256 threads = 4 waves in a 2 x 2 grid, each wave 64 x
 // 128 from 4 x 8 v_mfma_f32_16x16x32_bf16 tiles (128 fp32 accumulators per
 // lane). That leaves room for two blocks per CU (two waves per SIMD, 2 x 48 KB
 // of LDS): with one wave per SIMD nothing covers a wave's wait for global or
@@ -48,7 +49,7 @@ namespace moe {
 namespace {
 constexpr int BM = kPrefillBM;  // 128 rows (tokens / slots)
 constexpr int BN = 256;         // B rows staged per block
-constexpr int BK = 32;          // reduction step: a quarter of a quantization group
+constexpr int BK = 32;          // reduction step: within one quantization group
 constexpr int NT = 256;
 static_assert(BM == 128, "tile table row height");
 }  // namespace
@@ -165,8 +166,8 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         const int64_t rb = static_cast<int64_t>(tile.group) * (N / 16) + (bn >> 4);
         const uint8_t* q = (UP && tid >= 128) ? a.wq1 : a.wq0;
         const float* sc = (UP && tid >= 128) ? a.ws1 : a.ws0;
-        bq = q + rb * ng * 1024 + (bn & 15) * 64;  // + group * 1024 + quarter * 16
-        bs = sc + rb * ng * 16 + (bn & 15);          // + group * 16
+        bq = q + rb * ng * 1024 + (bn & 15) * 64;        // + tile * 1024 + quarter * 16
+        bs = sc + (rb * ng * 16 + (bn & 15)) * a.spt;   // + tile * 16 * spt + the step's group
     } else {
         const uint16_t* src;
         if (routed_rows)
@@ -192,7 +193,7 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         const int quarter = k & 3;
         if (ROUTED) {
             rb[0] = *reinterpret_cast<const u32x4*>(bq + g * 1024 + quarter * 16);
-            rs = bs[g * 16];
+            rs = bs[g * 16 * a.spt + ((quarter * a.spt) >> 2)];
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)

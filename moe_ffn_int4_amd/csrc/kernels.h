@@ -6,7 +6,9 @@
 
 namespace moe {
 
-// Quantization group: weights per fp32 scale.
+// Tile width of the tiled weight layouts (columns per 16-row tile), and the
+// default quantization group. Int4 groups of 64 or 32 weights keep the same
+// code tiles and store 128 / group scales per tile row.
 constexpr int kGroup = 128;
 
 // Largest expert count the router/top-k and dispatch kernels support.
@@ -24,7 +26,8 @@ constexpr int kSmallRouteLogits = 8192;
 constexpr int kSmallRoutePairs = 1024;
 
 // K1 (row-major groups, or the 16-row tiles the forward pass reads)
-hipError_t launch_quantize_int4(const float* w, int64_t rows, int64_t K, uint8_t* q,
+// group: 128, 64 or 32 weights per scale; K % 128 == 0
+hipError_t launch_quantize_int4(const float* w, int64_t rows, int64_t K, int group, uint8_t* q,
                                 float* scales, bool tiled, hipStream_t stream);
 // fp8 (E4M3) row-wise quantization: weights fp32 [rows, K] -> tiled codes
 // (16 x 128 tiles of 4 steps x 16 rows x 32 bytes) + per-row scales;
@@ -81,7 +84,8 @@ struct GroupedGemmArgs {
     const int32_t* counts;
     const int32_t* tile_base;
     const uint8_t* wq0;      // up: W1, down: W2 (int4, [E, N, K/2])
-    const float* ws0;        //   scales [E, N, K/128]
+    const float* ws0;        //   scales [E, N, K/group]
+    int spt;                 //   int4 scales per tile row: 128 / group (1, 2 or 4)
     const uint8_t* wq1;      // up: W3
     const float* ws1;
     const uint16_t* sh0;     // up: S1, down: S2 (bf16 [N, K])
@@ -112,6 +116,7 @@ struct DecodeArgs {
     int E;
     int64_t K;               // reduction dim
     int64_t N;               // output features
+    int spt;                 // int4 scales per tile row: 128 / group (1, 2 or 4)
     const int32_t* perm;
     const int4* chunks;      // (group, first row, rows, 0); rows index H / O
     const int32_t* nchunks;

@@ -2,21 +2,25 @@
 //
 // Computes int4_row_quantize as printed on the discosf.com page
 // "1 卡跑通 Llama 4", section "FP8 / Int4 混合量化": per group of 128
-// consecutive fp32 weights, scale = max(max|w|, 1e-6) / 8 and
-// code = clamp(round_half_even(w / scale), -8, 7).
+// consecutive fp32 weights (its group_size argument; 64 and 32 are the
+// smaller groups the lshu.cn page expects next), scale = max(max|w|, 1e-6) / 8
+// and code = clamp(round_half_even(w / scale), -8, 7).
 //
 // Bound by HBM: 4 bytes read and 0.5 + 4/128 bytes written per weight.
-// Mapping: one half-wave (32 lanes) per group, each lane one float4, so a
-// wave reads two whole groups (1 KB) in one fully coalesced load and writes
-// 2 x 64 bytes of packed codes. The group max is a 5-step xor-shuffle
-// reduction inside the half-wave. The division is IEEE correctly rounded (the
-// library is compiled with -fhip-fp32-correctly-rounded-divide-sqrt and no
-// fast-math), rintf maps to round-half-even, so codes and scales are
-// bit-identical to the fp32 definition.
+// Mapping: one half-wave (32 lanes) per 128 weights of a row, each lane one
+// float4, so a wave reads 1 KB in one fully coalesced load and writes 2 x 64
+// bytes of packed codes. A group's max is an xor-shuffle reduction over its
+// group / 4 lanes (5 steps for 128, 4 for 64, 3 for 32). The division is IEEE
+// correctly rounded (the library is compiled with
+// -fhip-fp32-correctly-rounded-divide-sqrt and no fast-math), rintf maps to
+// round-half-even, so codes and scales are bit-identical to the fp32
+// definition.
 //
 // TILED = true writes the storage order the forward pass reads: tile
-// t = (row/16) * (K/128) + group holds the group's 64 bytes for 16 rows
-// (1 KB) and its 16 scales, so one wavefront access covers one tile.
+// t = (row/16) * (K/128) + k/128 holds those 128 columns' 64 bytes for 16 rows
+// (1 KB) and their 16 x (128 / group) scales, scale s of row r at
+// t*16*S + (r%16)*S + s (S = 128 / group), so one wavefront access covers one
+// tile.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,8 +29,9 @@ namespace moe {
 template <bool TILED>
 __global__ __launch_bounds__(256) void quantize_int4_kernel(const float4* __restrict__ w,
                                                             int64_t ngroups, int64_t groups_per_row,
-                                                            uint16_t* __restrict__ q16,
+                                                            int group, uint16_t* __restrict__ q16,
                                                             float* __restrict__ scales) {
+    // ngroups / groups_per_row count 128-weight units; a unit holds S groups
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
     const int hl = lane & 31;
@@ -38,8 +43,7 @@ __global__ __launch_bounds__(256) void quantize_int4_kernel(const float4* __rest
         const bool valid = g < ngroups;
         float4 v = valid ? w[g * 32 + hl] : make_float4(0.f, 0.f, 0.f, 0.f);
         float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) {
+        for (int off = group >> 3; off >= 1; off >>= 1) {  // lanes of one group
             float o = __shfl_xor(m, off, 64);
             m = o > m ? o : m;
         }
@@ -53,30 +57,31 @@ __global__ __launch_bounds__(256) void quantize_int4_kernel(const float4* __rest
             packed |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xFu) << (4 * i);
         }
         if (valid) {
-            int64_t at = g;  // row-major: group g of the flattened [rows, K/128]
+            int64_t at = g;  // row-major: unit g of the flattened [rows, K/128]
             if (TILED) {
                 const int64_t r = g / groups_per_row, gg = g - r * groups_per_row;
                 at = ((r >> 4) * groups_per_row + gg) * 16 + (r & 15);
             }
             q16[at * 32 + hl] = static_cast<uint16_t>(packed);
-            if (hl == 0) scales[at] = s;
+            const int lanes = group >> 2, S = kGroup / group;
+            if (hl % lanes == 0) scales[at * S + hl / lanes] = s;
         }
     }
 }
 
-hipError_t launch_quantize_int4(const float* w, int64_t rows, int64_t K, uint8_t* q,
+hipError_t launch_quantize_int4(const float* w, int64_t rows, int64_t K, int group, uint8_t* q,
                                 float* scales, bool tiled, hipStream_t stream) {
     const int64_t ngroups = rows * (K / kGroup);
     if (ngroups == 0) return hipSuccess;
-    const int64_t want = (ngroups + 7) / 8;  // 8 groups per 256-thread block per pass
+    const int64_t want = (ngroups + 7) / 8;  // 8 units per 256-thread block per pass
     const int blocks = static_cast<int>(want < 8192 ? want : 8192);
     if (tiled)
         hipLaunchKernelGGL(quantize_int4_kernel<true>, dim3(blocks), dim3(256), 0, stream,
-                           reinterpret_cast<const float4*>(w), ngroups, K / kGroup,
+                           reinterpret_cast<const float4*>(w), ngroups, K / kGroup, group,
                            reinterpret_cast<uint16_t*>(q), scales);
     else
         hipLaunchKernelGGL(quantize_int4_kernel<false>, dim3(blocks), dim3(256), 0, stream,
-                           reinterpret_cast<const float4*>(w), ngroups, K / kGroup,
+                           reinterpret_cast<const float4*>(w), ngroups, K / kGroup, group,
                            reinterpret_cast<uint16_t*>(q), scales);
     return hipGetLastError();
 }

@@ -43,14 +43,16 @@ class Layer:
     experts_d: object        # moe.Int4Experts, moe.Bf16Experts or moe.Fp8Experts
     routed: str = "int4"     # routed expert weights: "int4", "bf16" or "fp8"
     act_ub: float = 0.0      # fp8 experts: activation scale bound
+    group: int = 128         # int4 experts: weights per scale
 
 
 def build_layer(cfg: W.MoEConfig, dev="cuda:0", routed_draw: Optional[str] = None,
-                routed: str = "int4", act_ub: float = W.FP8_ACT_UB) -> Layer:
+                routed: str = "int4", act_ub: float = W.FP8_ACT_UB, group: int = 128) -> Layer:
     """The layer on the GPU. Routed weights are drawn on the CPU for small
     layers and on the GPU (then quantized there) for the 5120 x 8192 ones.
     ``routed="bf16"`` keeps the routed experts in bf16 (RNE of the same draws);
-    ``routed="fp8"`` quantizes them to fp8 row-wise on the GPU (bound ``act_ub``)."""
+    ``routed="fp8"`` quantizes them to fp8 row-wise on the GPU (bound ``act_ub``);
+    int4 experts use groups of ``group`` weights per scale."""
     dev = torch.device(dev)
     if routed_draw is None:
         routed_draw = "cpu" if cfg.d * cfg.h <= 1 << 22 else str(dev)
@@ -62,7 +64,7 @@ def build_layer(cfg: W.MoEConfig, dev="cuda:0", routed_draw: Optional[str] = Non
     elif routed == "fp8":
         ex = moe.Fp8Experts.empty(cfg.E, cfg.d, cfg.h, dev, act_ub)
     else:
-        ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev)
+        ex = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, dev, group)
     for e in range(cfg.E):
         ws = [W.gen_expert_weight(cfg, w, e, routed_draw).to(dev) for w in ("w1", "w3", "w2")]
         if routed == "bf16":
@@ -74,7 +76,7 @@ def build_layer(cfg: W.MoEConfig, dev="cuda:0", routed_draw: Optional[str] = Non
     shared_d = moe.pack_shared(*(s.to(dev) for s in shared))
     torch.cuda.synchronize(dev)
     return Layer(cfg, x, wr, b, shared, routed_draw, dev, x.to(dev), wr.to(dev),
-                 None if b is None else b.to(dev), shared_d, ex, routed, float(act_ub))
+                 None if b is None else b.to(dev), shared_d, ex, routed, float(act_ub), int(group))
 
 
 def oracle_expert(layer: Layer, e: int):
@@ -94,7 +96,7 @@ def oracle_expert(layer: Layer, e: int):
     parts = []
     for w in ("w1", "w3", "w2"):
         wf = W.gen_expert_weight(layer.cfg, w, e, layer.gen_dev).cpu().numpy()
-        parts.extend(native.quantize_int4(wf))
+        parts.extend(native.quantize_int4(wf, layer.group))
         del wf
     return Int4Expert(*parts)
 
@@ -123,7 +125,7 @@ def oracle_forward_rows(layer: Layer, rows: np.ndarray, gpu_ids: Optional[np.nda
     for e in need:
         experts[e] = oracle_expert(layer, e)
     r = native.moe_forward_per_token(xs, layer.wr.numpy(), b, cfg.top_k, experts, layer.shared,
-                                     forced_ids=forced)
+                                     forced_ids=forced, group_size=layer.group)
     return r, margin
 
 

@@ -79,7 +79,8 @@ def _call_forward(L, dims, x=FAKE, wr=FAKE, b=None, experts=None, shared=None, y
     (dict(k=0), "top_k = 0"),
     (dict(E=4, k=5), "top_k = 5"),
     (dict(E=32, k=17), "top_k = 17"),
-    (dict(g=64), "group_size 64"),
+    (dict(g=16), "group_size 16"),
+    (dict(g=96), "group_size 96"),
 ])
 def test_invalid_dims(L, kw, needle):
     assert _call_forward(L, _dims(**kw), ws_bytes=1 << 40) == INVALID
@@ -136,7 +137,11 @@ def test_workspace_grows_with_the_layer(L):
 
 def test_quantize_validation(L):
     assert L.moe_quantize_int4(FAKE, 4, 100, 128, FAKE, FAKE, None) == INVALID
-    assert L.moe_quantize_int4(FAKE, 4, 256, 64, FAKE, FAKE, None) == INVALID
+    assert L.moe_quantize_int4(FAKE, 4, 256, 16, FAKE, FAKE, None) == INVALID
+    assert "group_size 16" in L.moe_last_error().decode()
+    assert L.moe_quantize_int4(FAKE, 4, 64, 32, FAKE, FAKE, None) == INVALID  # K % 128
+    assert L.moe_quantize_int4(FAKE, 0, 256, 64, FAKE, FAKE, None) == OK
+    assert L.moe_quantize_int4(FAKE, 0, 256, 32, FAKE, FAKE, None) == OK
     assert L.moe_quantize_int4(FAKE, -1, 256, 128, FAKE, FAKE, None) == INVALID
     assert L.moe_quantize_int4(None, 4, 256, 128, FAKE, FAKE, None) == INVALID
     assert L.moe_quantize_int4(FAKE, 4, 256, 128, None, FAKE, None) == INVALID

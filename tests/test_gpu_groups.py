@@ -1,0 +1,102 @@
+"""Int4 groups of 64 and 32 weights per scale on the GPU (the smaller group
+sizes the lshu.cn page, section "维护状态", expects next).
+
+* the quantizer, row-major and tiled, bit-exact against the oracle, with the
+  documented tiled scale address checked on raw memory;
+* the layer on every path against the oracle at the same group size, same
+  bar as the int4 layer at 128: every row within 2e-2 relative error
+  (infinity norm of the oracle's fp64 row), ids equal wherever the top-k
+  margin exceeds 1e-4; sampled rows of the Scout decode and prefill layers.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_ffn_int4_amd as moe
+import workloads as W
+from gpu_util import TOL, build_layer, check_ids, oracle_forward_rows, row_errors, sample_rows, say
+from oracle import int4_group_quantize
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GROUPS = [64, 32]
+
+
+@pytest.mark.parametrize("g", GROUPS)
+@pytest.mark.parametrize("rows,K", [(16, 128), (48, 384), (160, 5120)])
+def test_quantizer(g, rows, K):
+    say(f"quantize g={g}: rows={rows} K={K}")
+    rng = np.random.default_rng(rows + K + g)
+    w = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
+    w[3::7, :g] *= np.float32(1e-5)    # groups under the 1e-6 clamp
+    w[5::11, g:2 * g] *= np.float32(30.0)
+    c_ref, s_ref = int4_group_quantize(w, g)
+    wd = torch.from_numpy(w).to(DEV)
+    q, s = moe.quantize_int4(wd, group=g)
+    qt, st = moe.quantize_int4(wd, tiled=True, group=g)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(moe.unpack_int4(q.cpu()).numpy(), c_ref)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(moe.unpack_int4(moe.untile_int4(qt.cpu(), rows, K)).numpy(), c_ref)
+    np.testing.assert_array_equal(moe.untile_scales(st.cpu(), rows, K, g).numpy(), s_ref)
+    sb = st.cpu().numpy().reshape(-1)
+    S = 128 // g
+    for (r, k) in [(0, 0), (rows - 1, K - 1), (17 % rows, 130 % K), (rows // 2, K // 2 + 37)]:
+        t = (r // 16) * (K // 128) + k // 128
+        assert sb[(t * 16 + r % 16) * S + (k % 128) // g] == s_ref[r, k // g]
+
+
+def test_rejects_other_groups():
+    with pytest.raises(moe.MoEError, match="group_size"):
+        moe.quantize_int4(torch.zeros(16, 128, device=DEV), group=16)
+    with pytest.raises(ValueError):
+        moe.Int4Experts.empty(2, 128, 128, DEV, group=96)
+
+
+SMALL = {
+    "tiny": W.config(0),
+    "several tiles, ragged tail": W.config(0).with_(T=300, d=384, E=5, h=640, top_k=2),
+    "single token": W.config(0).with_(T=1, E=5, top_k=2),
+    "empty experts": W.config(0).with_(T=200, E=8, top_k=1, bias="zipf", bias_param=3.0),
+    "tile edge 257": W.config(0).with_(T=257, E=2, d=384, top_k=1),
+    "mixed expert sizes": W.config(0).with_(T=300, E=12, top_k=2, bias="zipf", bias_param=0.6),
+}
+
+
+def _run(layer, path="auto"):
+    cfg = layer.cfg
+    ids = torch.empty(cfg.T, cfg.top_k, dtype=torch.int32, device=DEV)
+    y = moe.forward(layer.x_d, layer.wr_d, layer.b_d, layer.experts_d, layer.shared_d,
+                    cfg.top_k, path=path, topk_ids=ids)
+    torch.cuda.synchronize()
+    return y.cpu(), ids.cpu().numpy()
+
+
+def _check(layer, y, ids, rows):
+    ref, margin = oracle_forward_rows(layer, rows, gpu_ids=ids)
+    ties = check_ids(ids[rows], ref.ids, margin)
+    err = row_errors(y[torch.as_tensor(rows)], ref.y)
+    say(f"  rows={len(rows)} ties={ties} max row rel err={err.max():.3e}")
+    assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("path", ["prefill", "decode", "hybrid"])
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("g", GROUPS)
+def test_small_layers_every_token(g, name, path):
+    cfg = SMALL[name]
+    say(f"forward g={g} [{path}]: {name} T={cfg.T} d={cfg.d} E={cfg.E} h={cfg.h} k={cfg.top_k}")
+    layer = build_layer(cfg, group=g)
+    y, ids = _run(layer, path)
+    _check(layer, y, ids, np.arange(cfg.T))
+
+
+@pytest.mark.parametrize("g", GROUPS)
+@pytest.mark.parametrize("i,nrows", [(1, 16), (2, 24)])
+def test_benchmark_layers_sampled(g, i, nrows):
+    cfg = W.config(i)
+    say(f"forward g={g}: config {i} ({cfg.name}), {nrows} rows")
+    layer = build_layer(cfg, group=g)
+    y, ids = _run(layer)
+    assert torch.isfinite(y.float()).all()
+    _check(layer, y, ids, sample_rows(cfg.T, nrows, seed=i))
