@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", type=int, default=1, help="benchmark layer 0..4 (default 1)")
     ap.add_argument("--layers", type=int, default=None, help="independent layer copies to cycle")
-    ap.add_argument("--path", default="auto", choices=["auto", "prefill", "decode", "hybrid"])
+    ap.add_argument("--path", default="auto", choices=["auto", "prefill", "decode", "hybrid", "prefill_wide"])
     ap.add_argument("--experts", default="int4", choices=["int4", "bf16", "fp8"],
                     help="routed expert weights: int4 g128 (default), bf16 (the baseline "
                          "path) or fp8 row-wise (the fp8_mixed path)")

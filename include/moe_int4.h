@@ -52,13 +52,17 @@ enum moe_status {
 
 enum moe_path {
     MOE_PATH_AUTO = 0,     /* DECODE for at most 64 token-expert pairs; HYBRID when the
-                              pairs average under 256 per routed expert; PREFILL otherwise */
-    MOE_PATH_PREFILL = 1,  /* grouped int4 GEMMs on MFMA for every expert */
+                              pairs average under 256 per routed expert; otherwise
+                              PREFILL_WIDE (PREFILL for fp8 experts) */
+    MOE_PATH_PREFILL = 1,  /* grouped GEMMs on MFMA for every expert, 128-row tiles */
     MOE_PATH_DECODE = 2,   /* HBM-streaming GEMV over the touched experts */
-    MOE_PATH_HYBRID = 3    /* grouped GEMMs for the shared expert and for routed experts with
+    MOE_PATH_HYBRID = 3,   /* grouped GEMMs for the shared expert and for routed experts with
                               more than 32 pairs; routed experts with 1..32 pairs on the
                               streaming kernel, which reads their weights once instead of
                               padding them to 128-row GEMM tiles */
+    MOE_PATH_PREFILL_WIDE = 4  /* PREFILL with 256 x 256 tiles (one block per CU, twice the
+                              MFMA work per fragment read); pays off when experts hold
+                              hundreds of rows. Not for fp8 experts (INVALID_ARG) */
 };
 
 /* Limits checked by validation. */
@@ -101,7 +105,8 @@ int moe_quantize_int4(const float *w, int64_t rows, int64_t K, int32_t group_siz
  * Tile (rb, g) covers rows 16*rb .. 16*rb+15 and reduction columns
  * 128*g .. 128*g+127; tiles are stored rb-major, t = rb * (K/128) + g. With
  * S = 128 / group_size scales per tile row:
- *   q       byte  t*1024 + (row % 16)*64 + (k % 128)/2   (low nibble = even k)
+ *   q       byte  t*1024 + ((k % 128)/32)*256 + (row % 16)*16 + (k % 32)/2
+ *           (low nibble = even k)
  *   scales  float (t*16 + row % 16)*S + (k % 128)/group_size
  * A wavefront reads one 1 KB tile (and its 64*S B of scales) per access.
  */

@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_int4.so")
 GROUP = 128                 # default int4 quantization group
 GROUPS = (128, 64, 32)      # supported int4 groups (weights per scale)
 TILE = 128                  # columns of a weight tile
-PATHS = {"auto": 0, "prefill": 1, "decode": 2, "hybrid": 3}
+PATHS = {"auto": 0, "prefill": 1, "decode": 2, "hybrid": 3, "prefill_wide": 4}
 
 MOE_OK = 0
 
@@ -490,7 +490,8 @@ def route(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tens
 
 def untile_int4(q: torch.Tensor, rows: int, K: int) -> torch.Tensor:
     """Tiled int4 bytes of one [rows, K] matrix -> row-major bytes [rows, K/2]."""
-    return q.reshape(rows // 16, K // TILE, 16, TILE // 2).permute(0, 2, 1, 3).reshape(rows, K // 2)
+    t = q.reshape(rows // 16, K // TILE, 4, 16, 16)  # row tile, k tile, step, row, byte
+    return t.permute(0, 3, 1, 2, 4).reshape(rows, K // 2)
 
 
 def untile_scales(s: torch.Tensor, rows: int, K: int, group: int = GROUP) -> torch.Tensor:

@@ -271,7 +271,7 @@ Routing carve(const moe_dims& d, void* ws) {
 // small_rows: which groups get streaming chunks and which GEMM tiles (build_work_lists)
 int run_routing(const moe_dims& d, const uint16_t* x, const float* wr, const float* b,
                 const Routing& R, int32_t* ids_out, float* gates_out, uint16_t* x_perm,
-                int small_rows, hipStream_t s) {
+                int small_rows, int tile_rows, hipStream_t s) {
     const moe::RouterPlan plan = moe::router_plan(d.T, d.d, d.E);
     CHECK(timed(MOE_STAGE_ROUTER, s, "router launch", [&] {
         return moe::launch_router_partials(x, wr, d.T, d.d, d.E, plan, R.partials, x_perm, s);
@@ -279,7 +279,7 @@ int run_routing(const moe_dims& d, const uint16_t* x, const float* wr, const flo
     if (small_routing(d)) {
         CHECK(timed(MOE_STAGE_TOPK, s, "small routing launch", [&] {
             return moe::launch_route_small(R.partials, plan.slices, b, d.T, d.E, d.top_k,
-                                           moe::kPrefillBM, small_rows, R.logits, R.ids, R.gates, ids_out,
+                                           tile_rows, small_rows, R.logits, R.ids, R.gates, ids_out,
                                            gates_out, R.counts, R.offsets, R.tile_base, R.perm,
                                            R.inv, R.chunks, R.nchunks, s);
         }));
@@ -290,7 +290,7 @@ int run_routing(const moe_dims& d, const uint16_t* x, const float* wr, const flo
                                 R.gates, ids_out, gates_out, s);
     }));
     CHECK(timed(MOE_STAGE_DISPATCH, s, "dispatch launch", [&] {
-        return moe::launch_dispatch(R.ids, d.T, d.top_k, d.E, moe::kPrefillBM, small_rows, R.counts, R.offsets,
+        return moe::launch_dispatch(R.ids, d.T, d.top_k, d.E, tile_rows, small_rows, R.counts, R.offsets,
                                     R.tile_base, R.perm, R.inv, R.chunks, R.nchunks, s);
     }));
     return MOE_OK;
@@ -432,7 +432,7 @@ int moe_route(const moe_dims* dims, const uint16_t* x, const float* router_w,
     const moe_dims& d = *dims;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Routing R = carve(d, workspace);
-    CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates, nullptr, 0, s));
+    CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates, nullptr, 0, moe::kPrefillBM, s));
     const size_t P = static_cast<size_t>(d.T) * d.top_k;
     if (logits)
         HIP_CHECK(hipMemcpyAsync(logits, R.logits, d.T * d.E * 4, hipMemcpyDeviceToDevice, s), "copy");
@@ -484,8 +484,10 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
     if (topk_ids) CHECK(check_ptr(topk_ids, "topk_ids", 4));
     if (topk_gates) CHECK(check_ptr(topk_gates, "topk_gates", 4));
     if (path != MOE_PATH_AUTO && path != MOE_PATH_PREFILL && path != MOE_PATH_DECODE &&
-        path != MOE_PATH_HYBRID)
+        path != MOE_PATH_HYBRID && path != MOE_PATH_PREFILL_WIDE)
         return fail(MOE_ERR_INVALID_ARG, "path %d unknown", path);
+    if (path == MOE_PATH_PREFILL_WIDE && ex8)
+        return fail(MOE_ERR_INVALID_ARG, "the 256-row GEMM tiles do not take fp8 experts");
     CHECK(device_ok());
 
     const moe_dims& d = *dims;
@@ -502,6 +504,10 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
     const bool hybrid = !decode && (path == MOE_PATH_HYBRID ||
                                     (path == MOE_PATH_AUTO && P < kHybridAvgPairs * d.E));
     const int small_rows = decode ? -1 : (hybrid ? kHybridRows : 0);
+    // 256 x 256 GEMM tiles: asked for, or (AUTO) the non-hybrid prefill of int4 / bf16 experts
+    const bool wide = !decode && !hybrid && !ex8 &&
+                      (path == MOE_PATH_PREFILL_WIDE || path == MOE_PATH_AUTO);
+    const int tile_rows = wide ? moe::kPrefillBM2 : moe::kPrefillBM;
     uint16_t* x_perm = reinterpret_cast<uint16_t*>(base + L.x_perm);
     uint8_t* xq = ex8 ? reinterpret_cast<uint8_t*>(base + L.xq) : nullptr;
     float* sxq = ex8 ? reinterpret_cast<float*>(base + L.sxq) : nullptr;
@@ -509,7 +515,7 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
     float* shq = ex8 ? reinterpret_cast<float*>(base + L.shq) : nullptr;
     // the interleaved copy of x feeds only the streaming kernel's int4 experts
     CHECK(run_routing(d, x, router_w, router_b, R, topk_ids, topk_gates,
-                      (decode || hybrid) && ex4 ? x_perm : nullptr, small_rows, s));
+                      (decode || hybrid) && ex4 ? x_perm : nullptr, small_rows, tile_rows, s));
     // fp8 experts: quantize x per row (the routed rows' A operand); H's routed
     // rows follow once the up-projections have written them
     if (ex8)
@@ -636,7 +642,9 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         g.sh0 = sh->s1;
         g.sh1 = sh->s3;
         g.h_out = H;
-        CHECK(timed(MOE_STAGE_UP, s, "grouped up launch", [&] { return moe::launch_grouped_up(g, s); }));
+        CHECK(timed(MOE_STAGE_UP, s, "grouped up launch", [&] {
+            return wide ? moe::launch_grouped_up256(g, s) : moe::launch_grouped_up(g, s);
+        }));
         const int hsplit = exb ? static_cast<int>(hybrid_chunks) : 0;
         if (hybrid) CHECK(stream_up(static_cast<int>(hybrid_chunks), hsplit));
         if (ex8) CHECK(quantize_h());
@@ -660,8 +668,9 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         g.sh1 = nullptr;
         g.h_out = nullptr;
         g.o_out = O;
-        CHECK(timed(MOE_STAGE_DOWN, s, "grouped down launch",
-                    [&] { return moe::launch_grouped_down(g, s); }));
+        CHECK(timed(MOE_STAGE_DOWN, s, "grouped down launch", [&] {
+            return wide ? moe::launch_grouped_down256(g, s) : moe::launch_grouped_down(g, s);
+        }));
         if (hybrid) CHECK(stream_down(static_cast<int>(hybrid_chunks), hsplit));
     }
 

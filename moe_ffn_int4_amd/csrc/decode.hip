@@ -61,14 +61,17 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
 }
 __device__ __forceinline__ float ld_stream_f(const float* p) { return __builtin_nontemporal_load(p); }
 
-// 8 two's-complement nibbles -> bf16 pairs (128 + u) in the order 0,4 | 1,5 | 2,6 | 3,7
+// 8 two's-complement nibbles -> bf16 pairs (128 + u) in the order 0,4 | 1,5 | 2,6 | 3,7.
+// u = code ^ 8 and the OR of 128.0 are one XOR with kMagic | 0x00080008 on the
+// masked nibbles (the magic's bits and the nibbles' do not overlap), so each
+// pair is a shift and one three-input bit operation.
 __device__ __forceinline__ uint4 offset_bf16(uint32_t w) {
-    const uint32_t u = w ^ 0x88888888u;
+    constexpr uint32_t kFlip = kMagic | 0x00080008u;
     uint4 r;
-    r.x = (u & 0x000F000Fu) | kMagic;
-    r.y = ((u >> 4) & 0x000F000Fu) | kMagic;
-    r.z = ((u >> 8) & 0x000F000Fu) | kMagic;
-    r.w = ((u >> 12) & 0x000F000Fu) | kMagic;
+    r.x = (w & 0x000F000Fu) ^ kFlip;
+    r.y = ((w >> 4) & 0x000F000Fu) ^ kFlip;
+    r.z = ((w >> 8) & 0x000F000Fu) ^ kFlip;
+    r.w = ((w >> 12) & 0x000F000Fu) ^ kFlip;
     return r;
 }
 
@@ -400,8 +403,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         constexpr int D = DL;
         constexpr int U = D + 1;
         const int64_t rb = static_cast<int64_t>(group) * (N / 16) + (n >> 4);
-        const uint8_t* q0 = a.wq0 + rb * ng * 1024 + l16 * 64 + kq * 16;
-        const uint8_t* q1 = UP ? a.wq1 + rb * ng * 1024 + l16 * 64 + kq * 16 : nullptr;
+        const uint8_t* q0 = a.wq0 + rb * ng * 1024 + kq * 256 + l16 * 16;
+        const uint8_t* q1 = UP ? a.wq1 + rb * ng * 1024 + kq * 256 + l16 * 16 : nullptr;
         const float* s0 = a.ws0 + (rb * ng * 16 + l16) * S;
         const float* s1 = UP ? a.ws1 + (rb * ng * 16 + l16) * S : nullptr;
         WeightSlot<S> sl[U];
@@ -433,8 +436,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         constexpr int U = D + 1;
         // tile row block of this lane's feature; tiles of a row block are consecutive
         const int64_t rb = static_cast<int64_t>(group) * (N / 16) + (n >> 4);
-        const uint8_t* q0 = a.wq0 + rb * ng * 1024 + l16 * 64 + kq * 16;
-        const uint8_t* q1 = UP ? a.wq1 + rb * ng * 1024 + l16 * 64 + kq * 16 : nullptr;
+        const uint8_t* q0 = a.wq0 + rb * ng * 1024 + kq * 256 + l16 * 16;
+        const uint8_t* q1 = UP ? a.wq1 + rb * ng * 1024 + kq * 256 + l16 * 16 : nullptr;
         const float* s0 = a.ws0 + (rb * ng * 16 + l16) * S;
         const float* s1 = UP ? a.ws1 + (rb * ng * 16 + l16) * S : nullptr;
         // Ring of U slots, group g in slot g % U. Loads past the last group re-read

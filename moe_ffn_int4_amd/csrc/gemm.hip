@@ -41,8 +41,7 @@
 // even). Accumulation is fp32 in the MFMA.
 #include <type_traits>
 
-#include "common.h"
-#include "kernels.h"
+#include "gemm_common.h"
 
 namespace moe {
 
@@ -53,50 +52,6 @@ constexpr int BK = 32;          // reduction step: within one quantization group
 constexpr int NT = 256;
 static_assert(BM == 128, "tile table row height");
 }  // namespace
-
-struct Tile {
-    int group;
-    int64_t row0;
-    int nrows;
-};
-
-__device__ __forceinline__ bool find_tile(const GroupedGemmArgs& a, int mt, Tile& t) {
-    const int G = a.E + 1;
-    if (mt >= a.tile_base[G]) return false;
-    int lo = 0, hi = G;  // tile_base[lo] <= mt < tile_base[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (a.tile_base[mid] <= mt) lo = mid;
-        else hi = mid;
-    }
-    const int local = mt - a.tile_base[lo];
-    int64_t start, count;
-    if (lo < a.E) {
-        start = a.offsets[lo];
-        count = a.counts[lo];
-    } else {
-        start = a.P;
-        count = a.T;
-    }
-    t.group = lo;
-    t.row0 = start + static_cast<int64_t>(local) * BM;
-    const int64_t left = count - static_cast<int64_t>(local) * BM;
-    t.nrows = static_cast<int>(left < BM ? left : BM);
-    return true;
-}
-
-// 8 int4 codes (one 32-bit word) times scale -> 4 packed bf16 pairs (RNE)
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const bf16x2 v = {static_cast<__bf16>(static_cast<float>(nib(w, 2 * j)) * s),
-                          static_cast<__bf16>(static_cast<float>(nib(w, 2 * j + 1)) * s)};
-        o[j] = __builtin_bit_cast(uint32_t, v);
-    }
-    return u32x4{o[0], o[1], o[2], o[3]};
-}
 
 // One block's tile: ROUTED picks the int4 or bf16 B source at compile time so
 // the reduction loop has no branches (a load under a branch is waited on where
@@ -117,9 +72,6 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s) {
 // the other LDS stage (int4 dequantized on the way); one barrier per step.
 // Loads are not issued under branches: a load under a branch is waited on
 // where the branch joins, which would serialize it with the MFMAs.
-__device__ __forceinline__ int frag_slot(int n, int q) {
-    return (q * 16 + (n ^ ((q * 4) ^ ((q >> 1) * 2)))) * 16;  // bytes in a sub-tile
-}
 
 template <bool UP, bool ROUTED>
 __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& tile, int nt,
@@ -154,29 +106,41 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
     // LDS byte offset of this thread's A piece i: sub-tile (tid/64) + 4 i
     const int a_st = (tid >> 6) * SUB + frag_slot((tid >> 2) & 15, tid & 3);
 
-    // ---- B staging: B row tid (pieces q = 0..3). Up: rows 0..127 are W1 rows
-    // n0 .. n0+127, rows 128..255 the same rows of W3; down: W2 rows n0+tid
-    // (the last down tile may reach past N: those rows re-read row N-1).
+    // ---- B staging. Up: B rows 0..127 are W1 rows n0 .. n0+127, rows
+    // 128..255 the same rows of W3; down: W2 rows n0 .. n0+255 (the last down
+    // tile may reach past N: those rows re-read valid rows, results dropped).
+    // int4: thread tid takes B row tid (32 codes per step; a wave reads four
+    // 256-byte step blocks); bf16: load c of a thread takes B tile (16 rows)
+    // 4 wave + c, lane -> row lane / 4, piece lane % 4 (one 1 KB step block).
     int64_t bn = UP ? n0 + (tid & 127) : n0 + tid;
     bn = bn < N ? bn : N - 1;
     const uint8_t* bq = nullptr;
     const float* bs = nullptr;
-    const uint16_t* bh = nullptr;
+    const uint16_t* bh[4] = {nullptr, nullptr, nullptr, nullptr};
+    const int wv = __builtin_amdgcn_readfirstlane(wid);
     if (ROUTED) {
         const int64_t rb = static_cast<int64_t>(tile.group) * (N / 16) + (bn >> 4);
         const uint8_t* q = (UP && tid >= 128) ? a.wq1 : a.wq0;
         const float* sc = (UP && tid >= 128) ? a.ws1 : a.ws0;
-        bq = q + rb * ng * 1024 + (bn & 15) * 64;        // + tile * 1024 + quarter * 16
+        bq = q + rb * ng * 1024 + (bn & 15) * 16;        // + tile * 1024 + quarter * 256
         bs = sc + (rb * ng * 16 + (bn & 15)) * a.spt;   // + tile * 16 * spt + the step's group
     } else {
-        const uint16_t* src;
-        if (routed_rows)
-            src = ((UP && tid >= 128) ? a.wb1 : a.wb0) + static_cast<int64_t>(tile.group) * N * K;
-        else
-            src = (UP && tid >= 128) ? a.sh1 : a.sh0;
-        bh = src + (bn >> 4) * ng * 2048 + (bn & 15) * 32;  // + group*2048 + quarter*512 + 8q
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int bt = wv * 4 + c;  // B tile 0..15
+            int64_t r0 = UP ? n0 + 16 * (bt & 7) : n0 + 16 * bt;
+            r0 = r0 < N ? r0 : N - 16;
+            const bool w3 = UP && bt >= 8;
+            const uint16_t* src;
+            if (routed_rows)
+                src = (w3 ? a.wb1 : a.wb0) + static_cast<int64_t>(tile.group) * N * K;
+            else
+                src = w3 ? a.sh1 : a.sh0;
+            bh[c] = src + (r0 >> 4) * ng * 2048 + lane * 8;  // + tile*2048 + quarter*512
+        }
     }
-    const int b_st = ASUB * SUB + (tid >> 4) * SUB;  // + frag_slot(tid & 15, q)
+    const int b_st = ASUB * SUB + (tid >> 4) * SUB;  // int4: + frag_slot(tid & 15, q)
+    const int b_st_h = ASUB * SUB + wv * 4 * SUB + frag_slot(lane >> 2, lane & 3);  // bf16: + c SUB
 
     constexpr int BV = ROUTED ? 1 : 4;
     // two register sets: global data two steps ahead of the MFMAs
@@ -192,12 +156,12 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         const int64_t g = k0 / kGroup;
         const int quarter = k & 3;
         if (ROUTED) {
-            rb[0] = *reinterpret_cast<const u32x4*>(bq + g * 1024 + quarter * 16);
+            rb[0] = *reinterpret_cast<const u32x4*>(bq + g * 1024 + quarter * 256);
             rs = bs[g * 16 * a.spt + ((quarter * a.spt) >> 2)];
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                rb[c] = *reinterpret_cast<const u32x4*>(bh + g * 2048 + quarter * 512 + c * 8);
+                rb[c] = *reinterpret_cast<const u32x4*>(bh[c] + g * 2048 + quarter * 512);
         }
     };
     // registers -> LDS stage (int4 B dequantized on the way)
@@ -208,8 +172,10 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         for (int i = 0; i < AP; ++i) *reinterpret_cast<u32x4*>(st + a_st + 4 * i * SUB) = ra[i];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const u32x4 v = ROUTED ? dequant8(rb[0][q], rs) : rb[ROUTED ? 0 : q];
-            *reinterpret_cast<u32x4*>(st + b_st + frag_slot(tid & 15, q)) = v;
+            if (ROUTED)
+                *reinterpret_cast<u32x4*>(st + b_st + frag_slot(tid & 15, q)) = dequant8(rb[0][q], rs);
+            else
+                *reinterpret_cast<u32x4*>(st + b_st_h + q * SUB) = rb[ROUTED ? 0 : q];
         }
     };
 
@@ -472,7 +438,7 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(GroupedGemmArgs a) 
     const int nt = (lin % span) / rows_here;
 
     Tile tile;
-    if (!find_tile(a, mt, tile)) return;
+    if (!find_tile<BM>(a, mt, tile)) return;
     if (tile.group < a.E && a.wf0) gemm_tile_fp8<UP>(a, tile, nt, lds);
     else if (tile.group < a.E && !a.wb0) gemm_tile<UP, true>(a, tile, nt, lds);
     else gemm_tile<UP, false>(a, tile, nt, lds);

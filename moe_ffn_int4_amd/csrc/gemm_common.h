@@ -1,0 +1,66 @@
+// gemm_common.h -- pieces shared by the grouped GEMM kernels (gemm.hip, gemm256.hip).
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// Row tile `mt` of the dispatch step's tile table (tile_base, BM rows per
+// tile): its group (routed experts 0..E-1, the shared expert E), first row and
+// row count. False past the last tile.
+struct Tile {
+    int group;
+    int64_t row0;
+    int nrows;
+};
+
+template <int BM>
+__device__ __forceinline__ bool find_tile(const GroupedGemmArgs& a, int mt, Tile& t) {
+    const int G = a.E + 1;
+    if (mt >= a.tile_base[G]) return false;
+    int lo = 0, hi = G;  // tile_base[lo] <= mt < tile_base[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.tile_base[mid] <= mt) lo = mid;
+        else hi = mid;
+    }
+    const int local = mt - a.tile_base[lo];
+    int64_t start, count;
+    if (lo < a.E) {
+        start = a.offsets[lo];
+        count = a.counts[lo];
+    } else {
+        start = a.P;
+        count = a.T;
+    }
+    t.group = lo;
+    t.row0 = start + static_cast<int64_t>(local) * BM;
+    const int64_t left = count - static_cast<int64_t>(local) * BM;
+    t.nrows = static_cast<int>(left < BM ? left : BM);
+    return true;
+}
+
+// 8 int4 codes (one 32-bit word) times scale -> 4 packed bf16 pairs (RNE)
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bf16x2 v = {static_cast<__bf16>(static_cast<float>(nib(w, 2 * j)) * s),
+                          static_cast<__bf16>(static_cast<float>(nib(w, 2 * j + 1)) * s)};
+        o[j] = __builtin_bit_cast(uint32_t, v);
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// MFMA fragment order of a 16-row x 32-column bf16 sub-tile (1 KB): the
+// 16-byte piece (row n, columns 8q .. 8q+7) sits at slot 16 q + (n ^ c[q]),
+// c = {0, 4, 10, 14}. A fragment read (lane -> n = lane % 16, q = lane / 16)
+// and a staging write (lane -> n = lane / 4, q = lane % 4) then touch distinct
+// banks in every group of 8 or 16 lanes.
+__device__ __forceinline__ int frag_slot(int n, int q) {
+    return (q * 16 + (n ^ ((q * 4) ^ ((q >> 1) * 2)))) * 16;  // bytes in a sub-tile
+}
+
+}  // namespace moe

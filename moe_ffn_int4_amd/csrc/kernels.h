@@ -14,9 +14,10 @@ constexpr int kGroup = 128;
 // Largest expert count the router/top-k and dispatch kernels support.
 constexpr int kMaxExperts = 256;
 
-// Tile height (token rows) of the prefill grouped GEMMs; the dispatch step
-// lays out its tile table for this height.
+// Tile heights (token rows) of the prefill grouped GEMMs; the dispatch step
+// lays out its tile table for the one the forward uses.
 constexpr int kPrefillBM = 128;
+constexpr int kPrefillBM2 = 256;  // 256 x 256 tiles (gemm256.hip) for large experts
 
 // Rows per decode chunk (the M of one MFMA tile).
 constexpr int kDecodeRows = 16;
@@ -106,6 +107,10 @@ struct GroupedGemmArgs {
 hipError_t launch_grouped_up(const GroupedGemmArgs& args, hipStream_t stream);
 // K5 (routed) + K6b (shared): O = H W2^T, one launch
 hipError_t launch_grouped_down(const GroupedGemmArgs& args, hipStream_t stream);
+// the same two launches with 256 x 256 tiles (tile table of kPrefillBM2 rows;
+// int4 or bf16 routed experts, not fp8)
+hipError_t launch_grouped_up256(const GroupedGemmArgs& args, hipStream_t stream);
+hipError_t launch_grouped_down256(const GroupedGemmArgs& args, hipStream_t stream);
 
 struct DecodeArgs {
     const uint16_t* a;       // up: x [T, d]; down: H [P + T, h]

@@ -17,10 +17,11 @@
 // definition.
 //
 // TILED = true writes the storage order the forward pass reads: tile
-// t = (row/16) * (K/128) + k/128 holds those 128 columns' 64 bytes for 16 rows
-// (1 KB) and their 16 x (128 / group) scales, scale s of row r at
-// t*16*S + (r%16)*S + s (S = 128 / group), so one wavefront access covers one
-// tile.
+// t = (row/16) * (K/128) + k/128 holds those 128 columns of 16 rows (1 KB) as
+// four 32-column steps of 16 rows x 16 bytes, and their 16 x (128 / group)
+// scales, scale s of row r at t*16*S + (r%16)*S + s (S = 128 / group): one
+// wavefront access covers one tile, one GEMM step of 16 rows is 256
+// contiguous bytes.
 #include "common.h"
 #include "kernels.h"
 
@@ -62,7 +63,10 @@ __global__ __launch_bounds__(256) void quantize_int4_kernel(const float4* __rest
                 const int64_t r = g / groups_per_row, gg = g - r * groups_per_row;
                 at = ((r >> 4) * groups_per_row + gg) * 16 + (r & 15);
             }
-            q16[at * 32 + hl] = static_cast<uint16_t>(packed);
+            // tiled: 32-column step (hl / 8) of the 16-row tile, then the row, then
+            // this lane's 4 codes; row-major: the row's 64 bytes in order
+            q16[TILED ? (at >> 4) * 512 + (hl >> 3) * 128 + (at & 15) * 8 + (hl & 7) : at * 32 + hl] =
+                static_cast<uint16_t>(packed);
             const int lanes = group >> 2, S = kGroup / group;
             if (hl % lanes == 0) scales[at * S + hl / lanes] = s;
         }

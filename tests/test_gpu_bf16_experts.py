@@ -40,7 +40,7 @@ def _check(layer, y, ids, rows):
     assert err.max() <= TOL
 
 
-@pytest.mark.parametrize("path", ["prefill", "decode", "hybrid"])
+@pytest.mark.parametrize("path", ["prefill", "decode", "hybrid", "prefill_wide"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_layers_every_token(name, path):
     cfg = SMALL[name]

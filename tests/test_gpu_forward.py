@@ -59,7 +59,7 @@ SMALL = {
 }
 
 
-@pytest.mark.parametrize("path", ["prefill", "decode", "hybrid"])
+@pytest.mark.parametrize("path", ["prefill", "decode", "hybrid", "prefill_wide"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_layers_every_token(name, path):
     cfg = SMALL[name]
@@ -72,7 +72,7 @@ def test_small_layers_every_token(name, path):
 def test_tiny_layer_all_paths_agree():
     layer = build_layer(W.config(0))
     y1, i1, _ = _run(layer, "prefill")
-    for other in ("decode", "hybrid"):
+    for other in ("decode", "hybrid", "prefill_wide"):
         y2, i2, _ = _run(layer, other)
         np.testing.assert_array_equal(i1, i2)
         err = row_errors(y1, y2.float().numpy().astype(np.float64))

@@ -99,5 +99,7 @@ def test_rejects_small_workspace_and_bad_bound():
         _run(layer, workspace=small)
     bad = moe.Fp8Experts(*(getattr(layer.experts_d, n) for n in
                            ("w1q", "w3q", "w2q", "w1s", "w3s", "w2s")), float("nan"))
+    with pytest.raises(moe.MoEError, match="fp8"):
+        _run(layer, path="prefill_wide")
     with pytest.raises(moe.MoEError, match="act_ub"):
         moe.forward(layer.x_d, layer.wr_d, layer.b_d, bad, layer.shared_d, cfg.top_k)

@@ -80,7 +80,7 @@ def _check(layer, y, ids, rows):
     assert err.max() <= TOL
 
 
-@pytest.mark.parametrize("path", ["prefill", "decode", "hybrid"])
+@pytest.mark.parametrize("path", ["prefill", "decode", "hybrid", "prefill_wide"])
 @pytest.mark.parametrize("name", list(SMALL))
 @pytest.mark.parametrize("g", GROUPS)
 def test_small_layers_every_token(g, name, path):

@@ -94,7 +94,7 @@ def test_tiled_layout_holds_the_same_codes(rows, K):
     c_ref, s_ref = int4_group_quantize(w)
     for (r, k) in [(0, 0), (rows - 1, K - 1), (17 % rows, 130 % K), (rows // 2, K // 2 + 3)]:
         t = (r // 16) * (K // 128) + k // 128
-        byte = int(qb[t * 1024 + (r % 16) * 64 + (k % 128) // 2])
+        byte = int(qb[t * 1024 + ((k % 128) // 32) * 256 + (r % 16) * 16 + (k % 32) // 2])
         nib = (byte >> 4) if k % 2 else (byte & 15)
         assert (nib - 16 if nib >= 8 else nib) == c_ref[r, k]
         assert sb[t * 16 + r % 16] == s_ref[r, k // 128]
