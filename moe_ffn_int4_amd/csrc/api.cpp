@@ -46,7 +46,7 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // Workspace sections (byte offsets from the workspace base).
 struct Layout {
     size_t partials, logits, ids, gates, counts, offsets, tile_base, perm, inv, chunks, nchunks,
-        routing_end, x_perm, H, O, total;
+        wparts, routing_end, x_perm, H, O, total;
     size_t xq, sxq, hq, shq, total_fp8;  // fp8 experts: quantized x and H rows, row scales
     int slices;
     int max_chunks;
@@ -81,6 +81,7 @@ Layout layout(const moe_dims& d) {
     L.inv = take(P * 4);
     L.chunks = take(static_cast<size_t>(L.max_chunks) * 16);
     L.nchunks = take(4);
+    L.wparts = take(plan.kind == 4 ? 3 * E * static_cast<size_t>(d.d) * 2 : 0);
     L.routing_end = off;
     L.x_perm = take(T * static_cast<size_t>(d.d) * 2);
     L.H = take((P + T) * static_cast<size_t>(d.h) * 2);
@@ -246,6 +247,7 @@ struct Routing {
     int32_t* inv;
     int4* chunks;
     int32_t* nchunks;
+    uint16_t* wparts;
 };
 
 Routing carve(const moe_dims& d, void* ws) {
@@ -263,7 +265,39 @@ Routing carve(const moe_dims& d, void* ws) {
     R.inv = reinterpret_cast<int32_t*>(b + L.inv);
     R.chunks = reinterpret_cast<int4*>(b + L.chunks);
     R.nchunks = reinterpret_cast<int32_t*>(b + L.nchunks);
+    R.wparts = reinterpret_cast<uint16_t*>(b + L.wparts);
     return R;
+}
+
+// The hybrid path's second stream: per device, a non-blocking stream of
+// default priority owned by the library (kept for the life of the process)
+// and the events that fork the small experts' streaming kernels off the
+// caller's stream and join them back. The fork and join of one call are
+// enqueued under the mutex, so calls from several host threads cannot
+// interleave their event records; the GPU work of such calls then shares the
+// side stream in enqueue order.
+struct Side {
+    std::mutex mu;
+    bool ready = false;
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, mid = nullptr, quant = nullptr, join = nullptr;
+};
+
+int side_stream(Side** out) {
+    static Side sides[64];
+    int dev = 0;
+    HIP_CHECK(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED_DEVICE, "device ordinal %d", dev);
+    Side& sd = sides[dev];
+    std::lock_guard<std::mutex> lock(sd.mu);
+    if (!sd.ready) {
+        HIP_CHECK(hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking), "hipStreamCreate");
+        for (hipEvent_t* e : {&sd.fork, &sd.mid, &sd.quant, &sd.join})
+            HIP_CHECK(hipEventCreateWithFlags(e, hipEventDisableTiming), "hipEventCreate");
+        sd.ready = true;
+    }
+    *out = &sd;
+    return MOE_OK;
 }
 
 // Router partial logits, then either the one-block small-batch finish (top-k,
@@ -274,7 +308,7 @@ int run_routing(const moe_dims& d, const uint16_t* x, const float* wr, const flo
                 int small_rows, int tile_rows, hipStream_t s) {
     const moe::RouterPlan plan = moe::router_plan(d.T, d.d, d.E);
     CHECK(timed(MOE_STAGE_ROUTER, s, "router launch", [&] {
-        return moe::launch_router_partials(x, wr, d.T, d.d, d.E, plan, R.partials, x_perm, s);
+        return moe::launch_router_partials(x, wr, d.T, d.d, d.E, plan, R.partials, x_perm, R.wparts, s);
     }));
     if (small_routing(d)) {
         CHECK(timed(MOE_STAGE_TOPK, s, "small routing launch", [&] {
@@ -530,7 +564,7 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
 
     // streaming projections over the chunk list: every group (decode path) or
     // the small routed experts (hybrid path)
-    auto stream_up = [&](int max_chunks, int shared_chunks) {
+    auto stream_up = [&](int max_chunks, int shared_chunks, hipStream_t st) {
         moe::DecodeArgs a{};
         a.T = d.T;
         a.P = P;
@@ -563,10 +597,10 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         a.sh0 = sh->s1;
         a.sh1 = sh->s3;
         a.h_out = H;
-        return timed(MOE_STAGE_DECODE_UP, s, "decode up launch",
-                     [&] { return moe::launch_decode_up(a, max_chunks, shared_chunks, s); });
+        return timed(MOE_STAGE_DECODE_UP, st, "decode up launch",
+                     [&] { return moe::launch_decode_up(a, max_chunks, shared_chunks, st); });
     };
-    auto stream_down = [&](int max_chunks, int shared_chunks) {
+    auto stream_down = [&](int max_chunks, int shared_chunks, hipStream_t st) {
         moe::DecodeArgs a{};
         a.T = d.T;
         a.P = P;
@@ -593,8 +627,8 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         }
         a.sh0 = sh->s2;
         a.o_out = O;
-        return timed(MOE_STAGE_DECODE_DOWN, s, "decode down launch",
-                     [&] { return moe::launch_decode_down(a, max_chunks, shared_chunks, s); });
+        return timed(MOE_STAGE_DECODE_DOWN, st, "decode down launch",
+                     [&] { return moe::launch_decode_down(a, max_chunks, shared_chunks, st); });
     };
     // hybrid: at most min(E, P) small experts of at most two 16-row chunks each
     const int64_t hybrid_chunks =
@@ -605,9 +639,9 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         // the list, or every chunk when the routed experts are bf16
         const int split = exb ? L.max_chunks
                               : static_cast<int>((d.T + moe::kDecodeRows - 1) / moe::kDecodeRows);
-        CHECK(stream_up(L.max_chunks, split));
+        CHECK(stream_up(L.max_chunks, split, s));
         if (ex8) CHECK(quantize_h());
-        CHECK(stream_down(L.max_chunks, split));
+        CHECK(stream_down(L.max_chunks, split, s));
     } else {
         moe::GroupedGemmArgs g{};
         g.T = d.T;
@@ -642,12 +676,38 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         g.sh0 = sh->s1;
         g.sh1 = sh->s3;
         g.h_out = H;
+        // hybrid: the small experts' streaming kernels (HBM-bound) run on the
+        // side stream beside the grouped GEMMs (MFMA-bound); the two chains
+        // touch disjoint rows of H and O. fp8 experts quantize all routed H
+        // rows in one step between the two projections, which joins them there.
+        const int hsplit = exb ? static_cast<int>(hybrid_chunks) : 0;
+        const int hch = static_cast<int>(hybrid_chunks);
+        Side* side = nullptr;
+        std::unique_lock<std::mutex> side_lock;
+        if (hybrid) {
+            CHECK(side_stream(&side));
+            side_lock = std::unique_lock<std::mutex>(side->mu);
+            HIP_CHECK(hipEventRecord(side->fork, s), "hipEventRecord");
+            HIP_CHECK(hipStreamWaitEvent(side->stream, side->fork, 0), "hipStreamWaitEvent");
+            CHECK(stream_up(hch, hsplit, side->stream));
+            if (ex8) {
+                HIP_CHECK(hipEventRecord(side->mid, side->stream), "hipEventRecord");
+            } else {
+                CHECK(stream_down(hch, hsplit, side->stream));
+            }
+        }
         CHECK(timed(MOE_STAGE_UP, s, "grouped up launch", [&] {
             return wide ? moe::launch_grouped_up256(g, s) : moe::launch_grouped_up(g, s);
         }));
-        const int hsplit = exb ? static_cast<int>(hybrid_chunks) : 0;
-        if (hybrid) CHECK(stream_up(static_cast<int>(hybrid_chunks), hsplit));
-        if (ex8) CHECK(quantize_h());
+        if (ex8) {
+            if (hybrid) HIP_CHECK(hipStreamWaitEvent(s, side->mid, 0), "hipStreamWaitEvent");
+            CHECK(quantize_h());
+            if (hybrid) {
+                HIP_CHECK(hipEventRecord(side->quant, s), "hipEventRecord");
+                HIP_CHECK(hipStreamWaitEvent(side->stream, side->quant, 0), "hipStreamWaitEvent");
+                CHECK(stream_down(hch, hsplit, side->stream));
+            }
+        }
 
         g.a = H;
         g.K = d.h;
@@ -671,7 +731,10 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         CHECK(timed(MOE_STAGE_DOWN, s, "grouped down launch", [&] {
             return wide ? moe::launch_grouped_down256(g, s) : moe::launch_grouped_down(g, s);
         }));
-        if (hybrid) CHECK(stream_down(static_cast<int>(hybrid_chunks), hsplit));
+        if (hybrid) {
+            HIP_CHECK(hipEventRecord(side->join, side->stream), "hipEventRecord");
+            HIP_CHECK(hipStreamWaitEvent(s, side->join, 0), "hipStreamWaitEvent");
+        }
     }
 
     CHECK(timed(MOE_STAGE_COMBINE, s, "combine launch", [&] {

@@ -5,9 +5,13 @@
 // (torch.topk there). The score is a sigmoid gate of the logit; selection is
 // on the logits (same order as the sigmoid), ties go to the lower expert id.
 //
-// Logits stay fp32 (the bf16 x widens exactly, router weights are fp32, fp32
-// FMA accumulation): the choice of experts must not move with a cheaper
-// precision, so this small GEMM runs on the vector ALUs, not on bf16 MFMA.
+// Logits stay fp32: the choice of experts must not move with a cheaper
+// precision. Small batches (decode) run this small GEMM on the vector ALUs
+// (the bf16 x widens exactly, fp32 FMA accumulation). Prefill batches run it
+// on bf16 MFMA without losing precision: each fp32 router weight is split
+// exactly into three bf16 parts (hi + mid + lo, every part the rounding of
+// what the previous parts leave), so each product x * part is exact and the
+// matrix cores sum x * w in fp32 (router_mfma_kernel).
 //
 // router_partials_kernel<TT, EE, MT, ME>: a 256-thread block computes a
 // TT-token x EE-expert tile over one slice of the reduction dimension; each
@@ -112,6 +116,21 @@ __global__ __launch_bounds__(256) void router_partials_kernel(const uint16_t* __
 
 RouterPlan router_plan(int64_t T, int64_t d, int64_t E) {
     RouterPlan p{};
+    if (T >= kRouterMfmaTokens) {
+        // bf16 MFMA on the split weights: one wave per 32 tokens x 16 or 32
+        // experts; slices of the reduction (multiples of 64 wide) until there
+        // are about 8192 waves (each wave's loads are latency-bound)
+        p.kind = 4;
+        p.tt = 32;
+        p.ee = E <= 16 ? 16 : 32;
+        const int64_t waves = ((T + 31) / 32) * ((E + p.ee - 1) / p.ee);
+        const int64_t want = (8192 + waves - 1) / waves;
+        int64_t s = 1;
+        for (int64_t c = 1; c <= d / 64; ++c)
+            if ((d / 64) % c == 0 && c <= want) s = c;
+        p.slices = static_cast<int>(s);
+        return p;
+    }
     if (T <= 16 && E <= 16) {
         p.kind = 0;
         p.tt = 16;
@@ -139,9 +158,158 @@ RouterPlan router_plan(int64_t T, int64_t d, int64_t E) {
     return p;
 }
 
+// fp32 router weights [E, d] -> three bf16 parts [3][E][d] with
+// hi + mid + lo == w exactly: hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid)
+// (each difference is exact in fp32, and what is left after mid fits 8 bits)
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr, int64_t n,
+                                                           uint16_t* __restrict__ parts) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const float w = wr[i];
+        const uint16_t hi = f32_to_bf16(w);
+        const float r1 = w - bf16_to_f32(hi);
+        const uint16_t mid = f32_to_bf16(r1);
+        const float r2 = r1 - bf16_to_f32(mid);
+        parts[i] = hi;
+        parts[n + i] = mid;
+        parts[2 * n + i] = f32_to_bf16(r2);
+    }
+}
+
+// One wave per 32-token x (16 JN)-expert tile over one slice of the
+// reduction: 2 x JN v_mfma_f32_16x16x32_bf16 tiles, three MFMAs per tile and
+// 32-wide step (one per weight part), with the next step's fragments loaded
+// before the current step's MFMAs. A fragments come straight from x, B
+// fragments from the split weights (rows past T or E re-read the last row;
+// not stored). Partial sums go to out[slice][t][e]. The waves also write
+// x_perm (when asked) for their slice's columns of the tile's tokens, rows
+// spread over the tile's n_et waves.
+template <int JN>
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ parts,
+                                                          int64_t T, int64_t d, int64_t E, int n_et,
+                                                          int64_t slice, float* __restrict__ out,
+                                                          uint16_t* __restrict__ x_perm) {
+    const int lane = threadIdx.x & 63;
+    const int64_t task = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t n_tt = (T + 31) / 32;
+    if (task >= n_tt * n_et) return;
+    const int64_t tt = task / n_et;
+    const int et = static_cast<int>(task % n_et);
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int64_t kb = static_cast<int64_t>(blockIdx.y) * slice;
+    const uint16_t* xr[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        int64_t t = tt * 32 + 16 * i + l16;
+        t = t < T ? t : T - 1;
+        xr[i] = x + t * d + kb + kq * 8;
+    }
+    const uint16_t* wp[JN][3];
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+        int64_t e = static_cast<int64_t>(et) * 16 * JN + 16 * j + l16;
+        e = e < E ? e : E - 1;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) wp[j][q] = parts + (q * E + e) * d + kb + kq * 8;
+    }
+    f32x4 acc[2][JN];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < JN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 a[2], b[JN][3], na[2], nb[JN][3];
+    auto load = [&](bf16x8 (&fa)[2], bf16x8 (&fb)[JN][3], int64_t k) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(xr[i] + k);
+#pragma unroll
+        for (int j = 0; j < JN; ++j)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) fb[j][q] = *reinterpret_cast<const bf16x8*>(wp[j][q] + k);
+    };
+    auto mma = [&](const bf16x8 (&fa)[2], const bf16x8 (&fb)[JN][3]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < JN; ++j)
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j][q], acc[i][j], 0, 0, 0);
+    };
+    // slice is a multiple of 64: steps come in pairs
+    load(a, b, 0);
+    for (int64_t k = 0; k < slice; k += 64) {
+        load(na, nb, k + 32);
+        mma(a, b);
+        load(a, b, k + 64 < slice ? k + 64 : k);  // past the end: a harmless re-read
+        mma(na, nb);
+    }
+    float* o = out + static_cast<int64_t>(blockIdx.y) * T * E;
+    // D[token][expert]: token row 4 kq + r of the 16 x 16 tile, expert column l16
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < JN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t t = tt * 32 + 16 * i + 4 * kq + r;
+                const int64_t e = static_cast<int64_t>(et) * 16 * JN + 16 * j + l16;
+                if (t < T && e < E) o[t * E + e] = acc[i][j][r];
+            }
+    if (x_perm) {
+        // this slice's columns of the tile's rows r = et, et + n_et, ...;
+        // (row, 8-column piece) pairs in lane order, four in flight per lane
+        const int nr = (32 - et + n_et - 1) / n_et;
+        const int64_t per_row = slice / 8;
+        const int64_t items = static_cast<int64_t>(nr) * per_row;
+        for (int64_t base = 0; base < items; base += 256) {
+            uint4 v[4];
+            int64_t at[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t it = base + u * 64 + lane;
+                const int64_t r = it / per_row;
+                const int64_t t = tt * 32 + et + r * n_et;
+                at[u] = (it < items && t < T) ? t * d + kb + (it - r * per_row) * 8 : -1;
+                v[u] = at[u] >= 0 ? *reinterpret_cast<const uint4*>(x + at[u]) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (at[u] < 0) continue;
+                uint4 w;
+                w.x = (v[u].x & 0xFFFFu) | (v[u].z << 16);
+                w.y = (v[u].x >> 16) | (v[u].z & 0xFFFF0000u);
+                w.z = (v[u].y & 0xFFFFu) | (v[u].w << 16);
+                w.w = (v[u].y >> 16) | (v[u].w & 0xFFFF0000u);
+                *reinterpret_cast<uint4*>(x_perm + at[u]) = w;
+            }
+        }
+    }
+}
+
 hipError_t launch_router_partials(const uint16_t* x, const float* wr, int64_t T, int64_t d,
                                   int64_t E, const RouterPlan& p, float* partials,
-                                  uint16_t* x_perm, hipStream_t stream) {
+                                  uint16_t* x_perm, uint16_t* wparts, hipStream_t stream) {
+    if (p.kind == 4) {
+        const int64_t n = E * d;
+        const int64_t want = (n + 255) / 256;
+        hipLaunchKernelGGL(router_split_kernel, dim3(static_cast<unsigned>(want < 4096 ? want : 4096)),
+                           dim3(256), 0, stream, wr, n, wparts);
+        const int64_t slice = d / p.slices;
+        if (E <= 16) {
+            const int64_t tasks = (T + 31) / 32;
+            hipLaunchKernelGGL((router_mfma_kernel<1>),
+                               dim3(static_cast<unsigned>((tasks + 3) / 4), static_cast<unsigned>(p.slices)),
+                               dim3(256), 0, stream, x, wparts, T, d, E, 1, slice, partials, x_perm);
+        } else {
+            const int n_et = static_cast<int>((E + 31) / 32);
+            const int64_t tasks = ((T + 31) / 32) * n_et;
+            hipLaunchKernelGGL((router_mfma_kernel<2>),
+                               dim3(static_cast<unsigned>((tasks + 3) / 4), static_cast<unsigned>(p.slices)),
+                               dim3(256), 0, stream, x, wparts, T, d, E, n_et, slice, partials, x_perm);
+        }
+        return hipGetLastError();
+    }
     dim3 grid(static_cast<unsigned>((T + p.tt - 1) / p.tt), static_cast<unsigned>((E + p.ee - 1) / p.ee),
               static_cast<unsigned>(p.slices));
     const int64_t slice = d / p.slices;
