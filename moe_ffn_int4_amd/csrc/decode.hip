@@ -558,7 +558,7 @@ hipError_t launch_decode_up(const DecodeArgs& args, int max_chunks, int shared_c
     if (args.wf0) return launch_decode<true, 3, 1, 7, true, 1>(args, max_chunks, shared_chunks, stream);
     if (args.spt == 2) return launch_decode<true, 3, 1, 5, false, 2>(args, max_chunks, shared_chunks, stream);
     if (args.spt == 4) return launch_decode<true, 2, 1, 4, false, 4>(args, max_chunks, shared_chunks, stream);
-    return launch_decode<true, 3, 1, 7, false, 1>(args, max_chunks, shared_chunks, stream);
+    return launch_decode<true, 3, 1, 5, false, 1>(args, max_chunks, shared_chunks, stream);
 }
 
 hipError_t launch_decode_down(const DecodeArgs& args, int max_chunks, int shared_chunks,

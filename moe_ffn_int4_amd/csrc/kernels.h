@@ -49,6 +49,8 @@ struct RouterPlan {
     int slices;  // reduction slices (split-K); partial sums [slices, T, E]
 };
 RouterPlan router_plan(int64_t T, int64_t d, int64_t E);
+// Most reduction slices of the MFMA router plan
+constexpr int kMaxRouterSlices = 16;
 // Batches of at least this many tokens compute the router logits on MFMA
 constexpr int64_t kRouterMfmaTokens = 256;
 // K2: partials[s][t][e] = sum over slice s of x[t, :] router_w[e, :]   (fp32)

@@ -126,7 +126,7 @@ RouterPlan router_plan(int64_t T, int64_t d, int64_t E) {
         const int64_t waves = ((T + 31) / 32) * ((E + p.ee - 1) / p.ee);
         const int64_t want = (8192 + waves - 1) / waves;
         int64_t s = 1;
-        for (int64_t c = 1; c <= d / 64; ++c)
+        for (int64_t c = 1; c <= d / 64 && c <= kMaxRouterSlices; ++c)
             if ((d / 64) % c == 0 && c <= want) s = c;
         p.slices = static_cast<int>(s);
         return p;
@@ -334,6 +334,31 @@ hipError_t launch_router_partials(const uint16_t* x, const float* wr, int64_t T,
     return hipGetLastError();
 }
 
+// sum_{s < slices} p[s * stride] in slice order, slices <= M: all M loads are
+// issued before the first add (rows past `slices` re-read the last one), so
+// the sum costs one memory latency instead of one per few slices
+template <int M>
+__device__ __forceinline__ float sum_slices_m(const float* p, int slices, int64_t stride) {
+    float v[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) v[j] = p[static_cast<int64_t>(j < slices ? j : slices - 1) * stride];
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < M; ++j) s = j < slices ? s + v[j] : s;
+    return s;
+}
+
+// any number of slices, in rounds of 16 (still in slice order)
+__device__ __forceinline__ float sum_slices(const float* p, int slices, int64_t stride) {
+    if (slices <= 1) return p[0];
+    if (slices <= 4) return sum_slices_m<4>(p, slices, stride);
+    float s = 0.0f;
+    for (int k = 0; k < slices; k += 16)
+        s += sum_slices_m<16>(p + static_cast<int64_t>(k) * stride, slices - k < 16 ? slices - k : 16,
+                              stride);
+    return s;
+}
+
 // One wave per token: sums the slices' partial logits (slice order) plus the
 // bias, then k rounds of a wave-wide arg-max over (logit, lower id first).
 __device__ __forceinline__ void topk_wave(const float* v_in, int64_t E, int top_k, int lane,
@@ -394,16 +419,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
     if (t >= T) return;  // wave-uniform; no block-wide barrier below
     for (int64_t e = lane; e < E; e += 64) {
-        float s = 0.0f;
-        int i = 0;
-        for (; i + 4 <= slices; i += 4) {  // independent loads, summed in slice order
-            float v[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = partials[(static_cast<int64_t>(i + j) * T + t) * E + e];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s += v[j];
-        }
-        for (; i < slices; ++i) s += partials[(static_cast<int64_t>(i) * T + t) * E + e];
+        float s = sum_slices(partials + t * E + e, slices, T * E);
         if (bias) s += bias[e];
         row[w][e] = s;
         logits[t * E + e] = s;
@@ -442,16 +458,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     const int64_t TE = T * E;
     const int P = static_cast<int>(T) * top_k;
     for (int64_t i = tid; i < TE; i += 256) {
-        float s = 0.0f;
-        int k = 0;
-        for (; k + 8 <= slices; k += 8) {  // 8 independent loads in flight, summed in order
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = partials[(k + j) * TE + i];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) s += v[j];
-        }
-        for (; k < slices; ++k) s += partials[k * TE + i];
+        float s = sum_slices(partials + i, slices, TE);
         if (bias) s += bias[i % E];
         lg[i] = s;
         logits[i] = s;
