@@ -442,7 +442,7 @@ hipError_t launch_topk(const float* partials, int slices, const float* bias, int
 // Small-batch routing in one block: logits (slice sums + bias), top-k and
 // gates, then the dispatch (counts, offsets, stable perm / inv) and the work
 // lists of the projections (build_work_lists). Used when T * E <= kSmallRouteLogits and T * top_k <= 1024.
-__global__ __launch_bounds__(256) void route_small_kernel(
+__global__ __launch_bounds__(1024) void route_small_kernel(
     const float* __restrict__ partials, int slices, const float* __restrict__ bias, int64_t T,
     int E, int top_k, int tile_rows, int small_rows, float* __restrict__ logits,
     int32_t* __restrict__ ids,
@@ -454,22 +454,40 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     __shared__ int sids[1024];
     __shared__ float sg[1024];
     __shared__ int cnt[kMaxExperts], off[kMaxExperts + 1];
+    __shared__ float part[4][1024];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t TE = T * E;
     const int P = static_cast<int>(T) * top_k;
-    for (int64_t i = tid; i < TE; i += 256) {
-        float s = sum_slices(partials + i, slices, TE);
-        if (bias) s += bias[i % E];
-        lg[i] = s;
-        logits[i] = s;
+    if (TE <= 1024) {
+        // four threads per logit, each a quarter of the slices (in order), then
+        // the quarters in order: one round of loads in flight instead of several
+        const int q = tid >> 8;
+        const int qs = (slices + 3) / 4;
+        const int s0 = q * qs, s1 = (s0 + qs < slices) ? s0 + qs : slices;
+        for (int64_t i = tid & 255; i < TE; i += 256)
+            part[q][i] = s1 > s0 ? sum_slices(partials + s0 * TE + i, s1 - s0, TE) : 0.0f;
+        __syncthreads();
+        for (int64_t i = tid; i < TE; i += 1024) {
+            float s = ((part[0][i] + part[1][i]) + part[2][i]) + part[3][i];
+            if (bias) s += bias[i % E];
+            lg[i] = s;
+            logits[i] = s;
+        }
+    } else {
+        for (int64_t i = tid; i < TE; i += 1024) {
+            float s = sum_slices(partials + i, slices, TE);
+            if (bias) s += bias[i % E];
+            lg[i] = s;
+            logits[i] = s;
+        }
     }
     __syncthreads();
-    for (int64_t t = w; t < T; t += 4)
+    for (int64_t t = w; t < T; t += 16)
         topk_wave(lg + t * E, E, top_k, lane, sids + t * top_k, sg + t * top_k,
                   ids_copy ? ids_copy + t * top_k : nullptr,
                   gates_copy ? gates_copy + t * top_k : nullptr);
     __syncthreads();
-    for (int p = tid; p < P; p += 256) {
+    for (int p = tid; p < P; p += 1024) {
         ids[p] = sids[p];
         gates[p] = sg[p];
     }
@@ -493,7 +511,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
         build_work_lists(cnt, off, E, T, P, tile_rows, small_rows, tile_base, chunks, nchunks);
     }
     __syncthreads();
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += 1024) {
         counts[e] = off[e + 1] - off[e];
         offsets[e] = off[e];
     }
@@ -505,7 +523,7 @@ hipError_t launch_route_small(const float* partials, int slices, const float* bi
                               int32_t* ids, float* gates, int32_t* ids_copy, float* gates_copy,
                               int32_t* counts, int32_t* offsets, int32_t* tile_base, int32_t* perm,
                               int32_t* inv, int4* chunks, int32_t* nchunks, hipStream_t stream) {
-    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(256), 0, stream, partials, slices, bias, T,
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(1024), 0, stream, partials, slices, bias, T,
                        static_cast<int>(E), top_k, tile_rows, small_rows, logits, ids, gates, ids_copy,
                        gates_copy, counts, offsets, tile_base, perm, inv, chunks, nchunks);
     return hipGetLastError();

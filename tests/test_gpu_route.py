@@ -83,3 +83,25 @@ def test_routing_is_deterministic():
     b, _ = _route(cfg)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_prefill_router_keeps_fp32_weights():
+    """Batches of 256+ tokens compute the logits on bf16 matrix cores from the
+    router weights split into three bf16 parts. With x = 1, d = 128 and weights
+    such as 2^-8 + 2^-16 + 2^-24 (one bit in each part), every partial sum is a
+    short binary fraction, so fp32 accumulation in any order gives the exact
+    logit; dropping any part of a weight moves a logit by at least 2^-17."""
+    T, d, E = 256, 128, 4
+    x = torch.ones(T, d, dtype=torch.bfloat16)
+    w = np.empty((E, d), dtype=np.float32)
+    w[0] = 2.0 ** -8 + 2.0 ** -16 + 2.0 ** -24        # hi, mid and lo all non-zero
+    w[1] = -(2.0 ** -8 + 2.0 ** -16)                  # hi and mid, negative
+    w[2] = 2.0 ** -9 + 2.0 ** -20                     # mid far below hi
+    w[3, ::2] = 2.0 ** -8 + 2.0 ** -24                # cancels to zero in pairs
+    w[3, 1::2] = -(2.0 ** -8 + 2.0 ** -24)
+    assert not np.all(w == torch.from_numpy(w).to(torch.bfloat16).float().numpy())
+    r = moe.route(x.to(DEV), torch.from_numpy(w).to(DEV), None, 1)
+    torch.cuda.synchronize()
+    got = r["logits"].cpu().numpy().astype(np.float64)
+    want = w.astype(np.float64).sum(axis=1)
+    np.testing.assert_array_equal(got, np.broadcast_to(want, got.shape))
