@@ -184,3 +184,78 @@ def test_python_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         moe.quantize_int4(torch.zeros(4, 128))
+
+
+# ---- fp8 and bf16 routed experts, group sizes, paths (validation only)
+
+def _call_fp8(L, dims, experts=None, ws_bytes=None, path=0, ub=0.0):
+    if experts is None:
+        experts = moe._ExpertsFp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ub)
+    shared = moe._Shared(FAKE, FAKE, FAKE)
+    if ws_bytes is None:
+        ws_bytes = L.moe_forward_fp8_workspace_bytes(ctypes.byref(dims)) or (1 << 40)
+    return L.moe_forward_fp8(ctypes.byref(dims), FAKE, FAKE, None, ctypes.byref(experts),
+                             ctypes.byref(shared), FAKE, None, None, path, FAKE * 16, ws_bytes, None)
+
+
+def test_fp8_workspace_is_larger_by_the_quantized_rows(L):
+    d = _dims(T=64, d=256, E=4, h=512, k=2)
+    base = L.moe_forward_workspace_bytes(ctypes.byref(d))
+    fp8 = L.moe_forward_fp8_workspace_bytes(ctypes.byref(d))
+    # x_q [T, d] + H_q [P, h] bytes and their fp32 row scales, each section 256-byte aligned
+    assert fp8 - base >= 64 * 256 + 128 * 512 + 64 * 4 + 128 * 4
+    assert L.moe_forward_fp8_workspace_bytes(ctypes.byref(_dims(T=0))) == 0
+
+
+def test_fp8_forward_validation(L):
+    d = _dims()
+    ex = moe._ExpertsFp8(FAKE, FAKE, None, FAKE, FAKE, FAKE, 1200.0)
+    assert _call_fp8(L, d, experts=ex) == INVALID
+    assert "w2q" in L.moe_last_error().decode()
+    for bad in (float("nan"), -1.0, float("inf")):
+        assert _call_fp8(L, d, ub=bad) == INVALID
+        assert "act_ub" in L.moe_last_error().decode()
+    need = L.moe_forward_fp8_workspace_bytes(ctypes.byref(d))
+    assert _call_fp8(L, d, ws_bytes=L.moe_forward_workspace_bytes(ctypes.byref(d))) == WORKSPACE
+    assert need > L.moe_forward_workspace_bytes(ctypes.byref(d))
+    assert _call_fp8(L, d, path=4) == INVALID  # no 256-row tiles for fp8 experts
+    assert "fp8" in L.moe_last_error().decode()
+    null = L.moe_forward_fp8(ctypes.byref(d), FAKE, FAKE, None, None, ctypes.byref(moe._Shared(FAKE, FAKE, FAKE)),
+                             FAKE, None, None, 0, FAKE * 16, need, None)
+    assert null == INVALID and "experts" in L.moe_last_error().decode()
+
+
+def test_bf16_forward_validation(L):
+    d = _dims()
+    ex = moe._ExpertsBf16(FAKE, None, FAKE)
+    r = L.moe_forward_bf16(ctypes.byref(d), FAKE, FAKE, None, ctypes.byref(ex),
+                           ctypes.byref(moe._Shared(FAKE, FAKE, FAKE)), FAKE, None, None, 0, FAKE * 16,
+                           L.moe_forward_workspace_bytes(ctypes.byref(d)), None)
+    assert r == INVALID and "w3" in L.moe_last_error().decode()
+
+
+@pytest.mark.parametrize("g", [128, 64, 32])
+def test_supported_group_sizes_pass_dims_validation(L, g):
+    assert L.moe_forward_workspace_bytes(ctypes.byref(_dims(g=g))) > 0
+
+
+def test_paths(L):
+    for p in (0, 1, 2, 3, 4):
+        # validation passes for every known path; without a GPU the device check fails next
+        assert _call_forward(L, _dims(), path=p) in (HIPERR, UNSUPPORTED, OK)
+    assert _call_forward(L, _dims(), path=5) == INVALID
+
+
+def test_binding_group_sizes():
+    import torch
+    ex = moe.Int4Experts(*(torch.empty(s, dtype=dt) for s, dt in [
+        ((2, 256, 64), torch.uint8), ((2, 256, 64), torch.uint8), ((2, 128, 128), torch.uint8),
+        ((2, 256, 4), torch.float32), ((2, 256, 4), torch.float32), ((2, 128, 8), torch.float32)]))
+    assert ex.group == 32 and ex.d == 128 and ex.h == 256
+    with pytest.raises(ValueError):
+        moe.Int4Experts.empty(2, 128, 256, "cpu", group=48)
+    t = torch.arange(32 * 4, dtype=torch.float32)
+    s = moe.untile_scales(t, 32, 256, 64)  # tiled (t*16 + row)*S + s  ->  row-major [rows, K/g]
+    assert s.shape == (32, 4)
+    # row 17, group 3: tile (1, 1), row 1, scale 1 of that tile -> ((1*2+1)*16 + 1)*2 + 1
+    assert s[17, 3].item() == ((1 * 2 + 1) * 16 + 1) * 2 + 1
