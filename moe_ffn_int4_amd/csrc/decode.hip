@@ -8,19 +8,24 @@
 //
 // Work: row chunks (<= 16 token rows of one group: the shared expert first,
 // the largest work item, then routed experts in id order) from the routing
-// step, times blocks of 64 output features. A 256-thread block is 4 waves;
-// each wave owns 16 output features and streams them over the whole reduction
-// dimension on its own (no LDS, no block barriers), keeping the next groups'
-// loads in flight in a register ring. v_mfma_f32_16x16x32_bf16 takes the
-// chunk's tokens as its 16 rows (absent rows are zero) and the features as
-// its 16 columns.
+// step, times blocks of 64 output features. A 256-thread block is 4 waves.
+// For int4 and fp8 experts each wave owns 16 output features and streams them
+// over the whole reduction dimension on its own, keeping the next tiles'
+// loads in flight in a register ring; chunks of a few rows first stage their
+// A rows in LDS once per block. bf16 chunks (the shared expert, bf16 experts)
+// carry four times the bytes of int4: four blocks share a 64-feature range,
+// each wave of a block streams a quarter of the reduction, and the four
+// partial sums are added in LDS in wave order. v_mfma_f32_16x16x32_bf16 takes
+// the chunk's tokens as its 16 rows (rows past the chunk repeat its last row;
+// their outputs are not stored) and the features as its 16 columns.
 //
 // Weights come in the tiled layouts of moe_quantize_int4_tiled /
-// moe_pack_bf16_tiled, so every weight access of a wave is one contiguous
-// 1 KB tile (plus 64 B of scales), read with non-temporal loads.
-// Int4 weights (routed experts): per 128-wide group a lane streams one 16-byte
+// moe_pack_bf16_tiled / moe_quantize_fp8_tiled, so every weight access of a
+// wave is one contiguous 1 KB block of a tile (int4 scales: 64 B per 16 rows
+// and scale column), read with non-temporal loads.
+// Int4 weights (routed experts): per 128-wide tile a lane streams one 16-byte
 // piece (32 codes) of its feature's row. Codes become bf16 (128 + u),
-// u = code + 8, by OR-ing offset-binary nibbles into the bit pattern of 128.0
+// u = code + 8, by placing offset-binary nibbles into the bit pattern of 128.0
 // (about one VALU op per code; gfx950 has no packed bf16 add to remove the
 // offset). The offset is removed exactly by one extra MFMA per 32-wide step
 // against a constant B of -136 (shared by W1 and W3): a group's accumulator

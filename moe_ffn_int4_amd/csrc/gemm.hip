@@ -9,9 +9,10 @@
 // symmetrically as code * scale
 // (lshu.cn page, section "量化环节": zero-points are all zero).
 //
-// One launch covers all groups: routed experts 0..E-1 (int4 weights, rows =
-// the expert's slots from the dispatch step) and the shared expert as group E
-// (bf16 weights, rows = all T tokens): row tiles of all groups (tile_base from
+// One launch covers all groups: routed experts 0..E-1 (int4 weights, or bf16
+// / fp8 for the other expert formats; rows = the expert's slots from the
+// dispatch step) and the shared expert as group E (bf16 weights, rows = all T
+// tokens): row tiles of all groups (tile_base from
 // the dispatch step) x column tiles. Block order is XCD-aware: blocks are
 // dealt round-robin to the 8 XCDs, so each XCD is given a contiguous range of
 // tiles, walked in groups of 8 row tiles x all column tiles; the 64 blocks an
@@ -25,14 +26,16 @@
 //   down: O[slot, m]  = (H W2^T)[m]                    (fp32 out)
 //
 // Block tile 128 rows x 256 B-rows, reduction step 32 (a quarter of a
-// 128-column weight tile, inside one quantization group); 256 threads = 4 waves in a 2 x 2 grid, each wave 64 x
-// 128 from 4 x 8 v_mfma_f32_16x16x32_bf16 tiles (128 fp32 accumulators per
-// lane). That leaves room for two blocks per CU (two waves per SIMD, 2 x 48 KB
+// 128-column weight tile, inside one quantization group); 256 threads = 4
+// waves in a 2 x 2 grid, each wave 64 x 128 from 4 x 8
+// v_mfma_f32_16x16x32_bf16 tiles (128 fp32 accumulators per lane). That leaves room for two blocks per CU (two waves per SIMD, 2 x 48 KB
 // of LDS): with one wave per SIMD nothing covers a wave's wait for global or
 // LDS data, with two the other block's MFMAs do. LDS holds two 24 KB stages in
 // a bank-conflict-free fragment order; global data for step k+1 is in flight
-// while step k's MFMAs run (pipeline described at gemm_tile). A partial row
-// tile still runs all its MFMAs on clamped rows (results dropped).
+// while step k's MFMAs run, and step k+2 is requested (pipeline described at
+// gemm_tile). A partial row tile still runs all its MFMAs on clamped rows
+// (results dropped). Layers whose experts hold hundreds of rows use the
+// 256 x 256 tiles of gemm256.hip instead.
 //
 // Weights come in the tiled layouts (moe_quantize_int4_tiled /
 // moe_pack_bf16_tiled). Int4 B rows are dequantized on the way into LDS:
@@ -58,18 +61,19 @@ static_assert(BM == 128, "tile table row height");
 // the branch joins). Rows past the group's end and B rows past N read a valid
 // clamped address; their results are dropped by the epilogue.
 //
-// LDS holds 2 stages of one 32-wide reduction step: 16 A sub-tiles then
+// LDS holds 2 stages of one 32-wide reduction step: 8 A sub-tiles then
 // 16 B sub-tiles, each 16 rows x 32 k = 1 KB in MFMA fragment order: the
 // 16-byte piece (row n, k 8q..8q+7) sits at slot 16 q + (n ^ c[q]), c = {0, 4,
 // 10, 14}. A fragment read (lane -> n = lane % 16, q = lane / 16) and a staging
 // write (lane -> n = lane / 4, q = lane % 4) then touch distinct banks in every
 // group of 8 or 16 lanes.
 //
-// Step k: the global loads of step k+1 are issued first; each wave then
-// reads all 16 of its fragments of step k from LDS before the first of its 64
-// MFMAs (the reads are forced ahead of the MFMAs, so LDS latency is paid once
-// per step, not once per fragment); then step k+1 goes from registers into
-// the other LDS stage (int4 dequantized on the way); one barrier per step.
+// Step k: the global loads of step k+2 are issued first, into the register
+// set that step k+1's data is not in; each wave then reads all 12 of its
+// fragments of step k from LDS before the first of its 32 MFMAs (the reads
+// are forced ahead of the MFMAs, so LDS latency is paid once per step, not
+// once per fragment); then step k+1 goes from registers into the other LDS
+// stage (int4 dequantized on the way); one barrier per step.
 // Loads are not issued under branches: a load under a branch is waited on
 // where the branch joins, which would serialize it with the MFMAs.
 
