@@ -441,7 +441,9 @@ hipError_t launch_topk(const float* partials, int slices, const float* bias, int
 // ------------------------------------------------------------------------
 // Small-batch routing in one block: logits (slice sums + bias), top-k and
 // gates, then the dispatch (counts, offsets, stable perm / inv) and the work
-// lists of the projections (build_work_lists). Used when T * E <= kSmallRouteLogits and T * top_k <= 1024.
+// lists of the projections, the same lists build_work_lists makes, with every
+// thread (a pair or an expert per thread). Used when T * E <= kSmallRouteLogits
+// and T * top_k <= 1024.
 __global__ __launch_bounds__(1024) void route_small_kernel(
     const float* __restrict__ partials, int slices, const float* __restrict__ bias, int64_t T,
     int E, int top_k, int tile_rows, int small_rows, float* __restrict__ logits,
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     __shared__ float lg[kSmallRouteLogits];
     __shared__ int sids[1024];
     __shared__ float sg[1024];
-    __shared__ int cnt[kMaxExperts], off[kMaxExperts + 1];
+    __shared__ int off[kMaxExperts];
     __shared__ float part[4][1024];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t TE = T * E;
@@ -491,31 +493,97 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
         ids[p] = sids[p];
         gates[p] = sg[p];
     }
-    if (tid == 0) {
-        for (int e = 0; e < E; ++e) cnt[e] = 0;
-        for (int p = 0; p < P; ++p) cnt[sids[p]]++;
-        int run = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = run;
-            run += cnt[e];
-        }
-        off[E] = run;
-        for (int e = 0; e < E; ++e) cnt[e] = 0;  // reuse as running rank
-        for (int p = 0; p < P; ++p) {
-            const int e = sids[p];
-            const int slot = off[e] + cnt[e]++;
-            perm[slot] = p;
-            inv[p] = slot;
-        }
-        // cnt[e] is back to expert e's pair count after the ranking loop
-        build_work_lists(cnt, off, E, T, P, tile_rows, small_rows, tile_base, chunks, nchunks);
+
+    // Dispatch with every thread, pair p = tid (P <= 1024). Inside a wave, one
+    // ballot per distinct expert gives each pair its rank among the wave's
+    // pairs of that expert, and the wave's count of it; the counts taken over
+    // the waves in order make the slots stable (pairs ascending per expert).
+    int* wcnt = reinterpret_cast<int*>(&part[0][0]);  // [16 waves][kMaxExperts]; part is dead
+    for (int i = tid; i < 16 * kMaxExperts; i += 1024) wcnt[i] = 0;
+    __syncthreads();
+    const bool has = tid < P;
+    const int my_e = has ? sids[tid] : -1;
+    int rank = 0;
+    for (uint64_t todo = __ballot(has); todo;) {
+        const int leader = __ffsll(static_cast<unsigned long long>(todo)) - 1;
+        const int e0 = __shfl(my_e, leader, 64);
+        const uint64_t m = __ballot(my_e == e0);
+        if (my_e == e0) rank = __popcll(m & ((1ull << lane) - 1));
+        if (lane == leader) wcnt[w * kMaxExperts + e0] = __popcll(m);
+        todo &= ~m;
     }
     __syncthreads();
-    for (int e = tid; e < E; e += 1024) {
-        counts[e] = off[e + 1] - off[e];
-        offsets[e] = off[e];
+
+    // Per expert (thread e < E <= 256, waves 0-3): its count, the waves' counts
+    // made exclusive prefixes, and the work lists' sizes by the rule of
+    // build_work_lists: streaming chunks of kDecodeRows pairs for chunked
+    // experts (all of them when small_rows < 0, else those with 1..small_rows
+    // pairs), GEMM tiles of tile_rows for the others (all when small_rows < 0).
+    int c = 0, nch = 0, ntl = 0;
+    if (tid < E) {
+        for (int v = 0; v < (P + 63) / 64; ++v) {
+            const int n = wcnt[v * kMaxExperts + tid];
+            wcnt[v * kMaxExperts + tid] = c;
+            c += n;
+        }
+        const bool chunked = small_rows < 0 || (c > 0 && c <= small_rows);
+        nch = chunked ? (c + kDecodeRows - 1) / kDecodeRows : 0;
+        ntl = (small_rows < 0 || !chunked) ? (c + tile_rows - 1) / tile_rows : 0;
     }
-    if (tid == 0) offsets[E] = off[E];
+    // inclusive scans of (c, nch, ntl) over threads 0..255: in each wave by
+    // shuffles, then the wave totals
+    __shared__ int wtot[3][4];
+    int ic = c, ich = nch, itl = ntl;
+    if (w < 4) {
+        for (int o = 1; o < 64; o <<= 1) {
+            const int a = __shfl_up(ic, o, 64), b = __shfl_up(ich, o, 64), t = __shfl_up(itl, o, 64);
+            if (lane >= o) {
+                ic += a;
+                ich += b;
+                itl += t;
+            }
+        }
+        if (lane == 63) {
+            wtot[0][w] = ic;
+            wtot[1][w] = ich;
+            wtot[2][w] = itl;
+        }
+    }
+    // the shared expert's chunks (every token) lead the chunk list when small_rows < 0
+    const int lead = small_rows < 0 ? static_cast<int>((T + kDecodeRows - 1) / kDecodeRows) : 0;
+    for (int i = tid; i < lead; i += 1024) {
+        const int r = i * kDecodeRows;
+        chunks[i] = make_int4(E, P + r, T - r < kDecodeRows ? static_cast<int>(T - r) : kDecodeRows, 0);
+    }
+    __syncthreads();
+    if (tid < E) {
+        for (int v = 0; v < w; ++v) {
+            ic += wtot[0][v];
+            ich += wtot[1][v];
+            itl += wtot[2][v];
+        }
+        const int oc = ic - c, och = lead + ich - nch, otl = itl - ntl;
+        off[tid] = oc;
+        counts[tid] = c;
+        offsets[tid] = oc;
+        tile_base[tid] = otl;
+        for (int i = 0; i < nch; ++i) {
+            const int r = i * kDecodeRows;
+            chunks[och + i] = make_int4(tid, oc + r, c - r < kDecodeRows ? c - r : kDecodeRows, 0);
+        }
+        if (tid == E - 1) {
+            offsets[E] = ic;
+            tile_base[E] = itl;
+            tile_base[E + 1] = itl + static_cast<int>((T + tile_rows - 1) / tile_rows);
+            *nchunks = lead + ich;
+        }
+    }
+    __syncthreads();
+    if (has) {
+        const int slot = off[my_e] + wcnt[w * kMaxExperts + my_e] + rank;
+        perm[slot] = tid;
+        inv[tid] = slot;
+    }
 }
 
 hipError_t launch_route_small(const float* partials, int slices, const float* bias, int64_t T,
