@@ -53,7 +53,7 @@ enum moe_status {
 enum moe_path {
     MOE_PATH_AUTO = 0,     /* DECODE for at most 64 token-expert pairs; HYBRID when the
                               pairs average under 256 per routed expert; otherwise
-                              PREFILL_WIDE (PREFILL for fp8 experts) */
+                              PREFILL_WIDE */
     MOE_PATH_PREFILL = 1,  /* grouped GEMMs on MFMA for every expert, 128-row tiles */
     MOE_PATH_DECODE = 2,   /* HBM-streaming GEMV over the touched experts */
     MOE_PATH_HYBRID = 3,   /* grouped GEMMs for the shared expert and for routed experts with
@@ -62,7 +62,7 @@ enum moe_path {
                               padding them to 128-row GEMM tiles */
     MOE_PATH_PREFILL_WIDE = 4  /* PREFILL with 256 x 256 tiles (one block per CU, twice the
                               MFMA work per fragment read); pays off when experts hold
-                              hundreds of rows. Not for fp8 experts (INVALID_ARG) */
+                              hundreds of rows */
 };
 
 /* Limits checked by validation. */

@@ -520,8 +520,6 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
     if (path != MOE_PATH_AUTO && path != MOE_PATH_PREFILL && path != MOE_PATH_DECODE &&
         path != MOE_PATH_HYBRID && path != MOE_PATH_PREFILL_WIDE)
         return fail(MOE_ERR_INVALID_ARG, "path %d unknown", path);
-    if (path == MOE_PATH_PREFILL_WIDE && ex8)
-        return fail(MOE_ERR_INVALID_ARG, "the 256-row GEMM tiles do not take fp8 experts");
     CHECK(device_ok());
 
     const moe_dims& d = *dims;
@@ -538,8 +536,8 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
     const bool hybrid = !decode && (path == MOE_PATH_HYBRID ||
                                     (path == MOE_PATH_AUTO && P < kHybridAvgPairs * d.E));
     const int small_rows = decode ? -1 : (hybrid ? kHybridRows : 0);
-    // 256 x 256 GEMM tiles: asked for, or (AUTO) the non-hybrid prefill of int4 / bf16 experts
-    const bool wide = !decode && !hybrid && !ex8 &&
+    // 256 x 256 GEMM tiles: asked for, or (AUTO) the non-hybrid prefill
+    const bool wide = !decode && !hybrid &&
                       (path == MOE_PATH_PREFILL_WIDE || path == MOE_PATH_AUTO);
     const int tile_rows = wide ? moe::kPrefillBM2 : moe::kPrefillBM;
     uint16_t* x_perm = reinterpret_cast<uint16_t*>(base + L.x_perm);

@@ -24,8 +24,8 @@
 // retires the reads of step k+1's stage before step k+2 (the next writer of
 // that stage is step k+3's data, stored in iteration k+1... after that barrier).
 //
-// Partial row tiles run all MFMAs on clamped rows (results dropped). Tiles
-// with fp8 weights are not handled here (the host uses the 128-row kernel).
+// Partial row tiles run all MFMAs on clamped rows (results dropped). Tiles of
+// fp8 experts run their own body (gemm256_tile_fp8).
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -286,19 +286,205 @@ __device__ __forceinline__ void gemm256_tile(const GroupedGemmArgs& a, const Til
     }
 }
 
-// XCD-aware block order as in gemm.hip (row tiles of 256 rows)
+// Routed tiles of fp8 experts (fp8 activation rows x fp8 weights): the
+// gfx950 scaled fp8 matrix instruction v_mfma_scale_f32_16x16x128_f8f6f4
+// with both operands E4M3 and unit block scales (exponent 127), twice the rate
+// of the 32-deep bf16 and fp8 instructions. One step is 128 deep. Lane
+// (n = l % 16, q = l / 16) of a 16-row operand holds row n, bytes 32q .. 32q + 31
+// of the step; A and B use the same assignment, so every product pairs equal
+// k whatever order the instruction sums in. That is the contiguous 32 bytes
+// at 32 l of a 16-row x 128-column tile of the fp8 weights, and the 32 bytes
+// at 32q of the step in an activation row: global loads arrive in fragment
+// order. A 16-row sub-tile takes 2 KB of LDS as two 1 KB halves (lane l's
+// bytes 0-15 at 16 l, 16-31 at 1024 + 16 l), so staging writes and fragment
+// reads are contiguous 1 KB per instruction. Two 64 KB stages: step k+1 is
+// stored into the other stage while step k is multiplied, and step k+2 is
+// requested into registers, paced between the products. Each wave: 128 x 128 from 8 x 8 products, 256
+// accumulators. The epilogue scales by both row scales and rounds to bf16
+// where the fp8 matmul of the pages returns bf16: the two up-projections, then
+// the SwiGLU product (bf16 H); down: the expert output.
+constexpr int FSUB2 = 2048;               // bytes per 16-row x 128-column fp8 sub-tile
+constexpr int FSTAGE2 = 32 * FSUB2;       // 16 A + 16 B sub-tiles: 64 KB
+constexpr int NFSTAGE2 = 2;
+
 template <bool UP>
+__device__ __forceinline__ void gemm256_tile_fp8(const GroupedGemmArgs& a, const Tile& tile, int nt,
+                                                 uint8_t* lds) {
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    constexpr int FK = 128;
+    const int64_t K = a.K, N = a.N;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int wm = wid >> 1, wn = wid & 1;
+    const int r16 = lane & 15, q4 = lane >> 4;
+    const int64_t n0 = static_cast<int64_t>(nt) * (UP ? BN2 / 2 : BN2);
+    const int64_t ng = K / kGroup;
+    const int steps = static_cast<int>(K / FK);
+
+    // ---- staging: this wave takes A sub-tiles 4 wid + i (rows 64 wid + 16 i + r16)
+    // and B sub-tiles 4 wid + i (B rows 16 (4 wid + i) + r16), lane l's 32 bytes of each
+    const uint8_t* arow[4];
+    const uint8_t* brow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int r = 64 * wid + 16 * i + r16;
+        r = r < tile.nrows ? r : tile.nrows - 1;
+        const int64_t s = tile.row0 + r;
+        const int64_t src = UP ? a.perm[s] / a.top_k : s;
+        arow[i] = a.a8 + src * K + 32 * q4;
+        const int br = 16 * (4 * wid + i) + r16;
+        int64_t bn = UP ? n0 + (br & 127) : n0 + br;
+        bn = bn < N ? bn : N - 1;
+        const uint8_t* m = ((UP && br >= 128) ? a.wf1 : a.wf0) + static_cast<int64_t>(tile.group) * N * K;
+        brow[i] = m + (bn >> 4) * ng * 2048 + (bn & 15) * 32 + 512 * q4;  // + step * 2048
+    }
+    u32x4 ra[4][2], rb[4][2];
+    auto load_step = [&](int k) __attribute__((always_inline)) {
+        k = k < steps ? k : steps - 1;  // past the end: reload the last step (unused)
+        const int64_t ka = static_cast<int64_t>(k) * FK, kb = static_cast<int64_t>(k) * 2048;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                ra[i][h] = *reinterpret_cast<const u32x4*>(arow[i] + ka + 16 * h);
+                rb[i][h] = *reinterpret_cast<const u32x4*>(brow[i] + kb + 16 * h);
+            }
+    };
+    auto store_step = [&](int stage) __attribute__((always_inline)) {
+        uint8_t* st = lds + stage * FSTAGE2 + lane * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                *reinterpret_cast<u32x4*>(st + (4 * wid + i) * FSUB2 + h * 1024) = ra[i][h];
+                *reinterpret_cast<u32x4*>(st + (16 + 4 * wid + i) * FSUB2 + h * 1024) = rb[i][h];
+            }
+    };
+    auto frag = [&](const uint8_t* st, int sub) __attribute__((always_inline)) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(st + sub * FSUB2);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(st + sub * FSUB2 + 1024);
+        return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
+                     static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
+                     static_cast<int>(hi.z), static_cast<int>(hi.w)};
+    };
+    int sb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sb[j] = 16 + (UP ? ((j < 4) ? wn * 4 + j : 8 + wn * 4 + (j - 4)) : wn * 8 + j);
+
+    f32x4 acc[8][8];
+    // Step k: 8 chunks, one per B fragment j: its 8 products, the read of
+    // fragment j+1, and one staging piece of step k+1 (A and B sub-tile j / 2,
+    // half j % 2) written into the other stage, its registers then requested
+    // again for step k+2 (one step ahead of their next store). At the last step
+    // the piece goes to the idle stage and the request re-reads the last step.
+    // The first step starts the accumulators from zero (peeled, so that the
+    // loop-carried accumulators keep one register assignment).
+    auto step = [&](int k, auto first) __attribute__((always_inline)) {
+        constexpr bool FIRST = decltype(first)::value;
+        const uint8_t* st = lds + (k & 1) * FSTAGE2 + lane * 16;
+        uint8_t* wst = lds + ((k & 1) ^ 1) * FSTAGE2 + lane * 16;
+        const int kn = k + 2 < steps ? k + 2 : steps - 1;
+        const int64_t ka = static_cast<int64_t>(kn) * FK, kb = static_cast<int64_t>(kn) * 2048;
+        i32x8 fa[8], fb[2];
+        fb[0] = frag(st, sb[0]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fa[i] = frag(st, wm * 8 + i);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j + 1 < 8) fb[(j + 1) & 1] = frag(st, sb[j + 1]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fa[i], fb[j & 1], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i][j], 0, 0, 0, 127, 0, 127);
+            const int p = j >> 1, h = j & 1;
+            *reinterpret_cast<u32x4*>(wst + (4 * wid + p) * FSUB2 + h * 1024) = ra[p][h];
+            *reinterpret_cast<u32x4*>(wst + (16 + 4 * wid + p) * FSUB2 + h * 1024) = rb[p][h];
+            ra[p][h] = *reinterpret_cast<const u32x4*>(arow[p] + ka + 16 * h);
+            rb[p][h] = *reinterpret_cast<const u32x4*>(brow[p] + kb + 16 * h);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next fragment's reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // staging writes
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global loads
+            __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+    };
+
+    load_step(0);
+    store_step(0);
+    __syncthreads();
+    load_step(1);
+    step(0, std::true_type{});
+    for (int k = 1; k < steps; ++k) step(k, std::false_type{});
+
+    // ---- epilogue: D[row][col], row = 4 * lq + r inside a 16 x 16 sub-tile, col = l16
+    const int l16 = lane & 15, lq = lane >> 4;
+    const float* ws0 = a.wfs0 + static_cast<int64_t>(tile.group) * N;
+    const float* ws1 = UP ? a.wfs1 + static_cast<int64_t>(tile.group) * N : nullptr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = wm * 128 + i * 16 + lq * 4 + r;
+            if (row >= tile.nrows) continue;
+            const int64_t orow = tile.row0 + row;
+            const float sa = a.a8s[UP ? a.perm[orow] / a.top_k : orow];
+            if (UP) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t col = n0 + wn * 64 + j * 16 + l16;
+                    const float g = bf16_to_f32(f32_to_bf16(acc[i][j][r] * sa * ws0[col]));
+                    const float u = bf16_to_f32(f32_to_bf16(acc[i][j + 4][r] * sa * ws1[col]));
+                    a.h_out[orow * N + col] = f32_to_bf16(siluf_(g) * u);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t col = n0 + wn * 128 + j * 16 + l16;
+                    if (col < N) a.o_out[orow * N + col] = bf16_to_f32(f32_to_bf16(acc[i][j][r] * sa * ws0[col]));
+                }
+            }
+        }
+    }
+}
+
+// Relative time of one routed tile in eighths of a shared-expert (bf16) tile,
+// measured on the Scout prefill layer: int4 tiles dequantize their weights
+// (about 1.27), fp8 tiles run the fp8 instruction at twice the rate (about
+// 0.72), bf16 tiles match the shared expert's.
+__host__ __device__ constexpr int routed_tile_weight(bool f8, bool bf16) { return f8 ? 6 : (bf16 ? 8 : 10); }
+constexpr int kSharedTileWeight = 8;
+
+// XCD-aware block order as in gemm.hip (row tiles of 256 rows), except that
+// each XCD's contiguous range of tiles is cut by estimated time rather than
+// by count: the tile table lists the routed tiles first and the shared
+// expert's after them, and the two kinds differ in cost, so equal counts
+// would leave the XCDs holding the cheaper kind idle at the end. The grid has
+// slots for the largest range an XCD can get; the rest exit at once.
+// F8: launches with fp8 routed experts, a separate instantiation so that the
+// int4 / bf16 one keeps its register allocation and schedule.
+template <bool UP, bool F8>
 __global__ __launch_bounds__(NT2, 1) void grouped_gemm256_kernel(GroupedGemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int ncol = UP ? static_cast<int>(a.N / (BN2 / 2)) : static_cast<int>((a.N + BN2 - 1) / BN2);
     const int nrow = a.tile_base[a.E + 1];
-    const int total = nrow * ncol;
     const int L = blockIdx.x;
-    if (L >= total) return;
     constexpr int kXcd = 8, kGroupRows = 4;
     const int xcd = L % kXcd, slot = L / kXcd;
-    const int base = total / kXcd, extra = total % kXcd;
-    const int lin = xcd * base + (xcd < extra ? xcd : extra) + slot;
+    const int64_t wr = routed_tile_weight(F8, a.wb0 != nullptr);
+    const int64_t routed = static_cast<int64_t>(a.tile_base[a.E]) * ncol;  // tiles
+    const int64_t cr = routed * wr;
+    const int64_t cost = cr + (static_cast<int64_t>(nrow) * ncol - routed) * kSharedTileWeight;
+    // first tile of the XCD whose share of the cost starts at c
+    auto tile_at = [&](int64_t c) {
+        return c <= cr ? (c + wr - 1) / wr : routed + (c - cr + kSharedTileWeight - 1) / kSharedTileWeight;
+    };
+    const int64_t first = tile_at(cost * xcd / kXcd);
+    if (first + slot >= tile_at(cost * (xcd + 1) / kXcd)) return;
+    const int lin = static_cast<int>(first + slot);
     const int span = kGroupRows * ncol;
     const int first_row = (lin / span) * kGroupRows;
     const int rows_here = nrow - first_row < kGroupRows ? nrow - first_row : kGroupRows;
@@ -307,7 +493,8 @@ __global__ __launch_bounds__(NT2, 1) void grouped_gemm256_kernel(GroupedGemmArgs
 
     Tile tile;
     if (!find_tile<BM2>(a, mt, tile)) return;
-    if (tile.group < a.E && !a.wb0) gemm256_tile<UP, true>(a, tile, nt, lds);
+    if (F8 && tile.group < a.E) gemm256_tile_fp8<UP>(a, tile, nt, lds);
+    else if (!F8 && tile.group < a.E && !a.wb0) gemm256_tile<UP, true>(a, tile, nt, lds);
     else gemm256_tile<UP, false>(a, tile, nt, lds);
 }
 
@@ -316,28 +503,37 @@ static unsigned max_row_tiles256(const GroupedGemmArgs& a) {
     return static_cast<unsigned>((a.P + BM2 - 1) / BM2 + e_bound + (a.T + BM2 - 1) / BM2);
 }
 
-static constexpr size_t kGemm256Lds = NSTAGE2 * STAGE2;  // 96 KB
+// 96 KB for bf16 / int4 tiles, 128 KB when fp8 tiles are in the launch
+static constexpr size_t kGemm256Lds = NSTAGE2 * STAGE2;
+static constexpr size_t kGemm256LdsFp8 = NFSTAGE2 * FSTAGE2;
 
-template <bool UP>
-static hipError_t allow_lds256() {
+template <bool UP, bool F8>
+static hipError_t launch256(const GroupedGemmArgs& a, unsigned ncol, hipStream_t stream) {
+    constexpr size_t lds = F8 ? kGemm256LdsFp8 : kGemm256Lds;
     static hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&grouped_gemm256_kernel<UP>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGemm256Lds));
-    return e;
+        reinterpret_cast<const void*>(&grouped_gemm256_kernel<UP, F8>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    // an XCD's share of the cost, at most max_tiles * max weight / 8, in
+    // tiles of the lightest kind, plus one for rounding
+    const int64_t wr = routed_tile_weight(F8, a.wb0 != nullptr);
+    const int64_t wmax = wr > kSharedTileWeight ? wr : kSharedTileWeight;
+    const int64_t wmin = wr < kSharedTileWeight ? wr : kSharedTileWeight;
+    const int64_t tiles = static_cast<int64_t>(max_row_tiles256(a)) * ncol;
+    const int64_t slots = (tiles * wmax + 8 * wmin - 1) / (8 * wmin) + 1;
+    dim3 grid(static_cast<unsigned>(8 * slots));
+    hipLaunchKernelGGL((grouped_gemm256_kernel<UP, F8>), grid, dim3(NT2), lds, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_grouped_up256(const GroupedGemmArgs& a, hipStream_t stream) {
-    if (hipError_t e = allow_lds256<true>(); e != hipSuccess) return e;
-    dim3 grid(max_row_tiles256(a) * static_cast<unsigned>(a.N / (BN2 / 2)));
-    hipLaunchKernelGGL(grouped_gemm256_kernel<true>, grid, dim3(NT2), kGemm256Lds, stream, a);
-    return hipGetLastError();
+    const unsigned ncol = static_cast<unsigned>(a.N / (BN2 / 2));
+    return a.wf0 ? launch256<true, true>(a, ncol, stream) : launch256<true, false>(a, ncol, stream);
 }
 
 hipError_t launch_grouped_down256(const GroupedGemmArgs& a, hipStream_t stream) {
-    if (hipError_t e = allow_lds256<false>(); e != hipSuccess) return e;
-    dim3 grid(max_row_tiles256(a) * static_cast<unsigned>((a.N + BN2 - 1) / BN2));
-    hipLaunchKernelGGL(grouped_gemm256_kernel<false>, grid, dim3(NT2), kGemm256Lds, stream, a);
-    return hipGetLastError();
+    const unsigned ncol = static_cast<unsigned>((a.N + BN2 - 1) / BN2);
+    return a.wf0 ? launch256<false, true>(a, ncol, stream) : launch256<false, false>(a, ncol, stream);
 }
 
 }  // namespace moe

@@ -218,8 +218,8 @@ def test_fp8_forward_validation(L):
     need = L.moe_forward_fp8_workspace_bytes(ctypes.byref(d))
     assert _call_fp8(L, d, ws_bytes=L.moe_forward_workspace_bytes(ctypes.byref(d))) == WORKSPACE
     assert need > L.moe_forward_workspace_bytes(ctypes.byref(d))
-    assert _call_fp8(L, d, path=4) == INVALID  # no 256-row tiles for fp8 experts
-    assert "fp8" in L.moe_last_error().decode()
+    assert _call_fp8(L, d, path=5) == INVALID
+    assert "path" in L.moe_last_error().decode()
     null = L.moe_forward_fp8(ctypes.byref(d), FAKE, FAKE, None, None, ctypes.byref(moe._Shared(FAKE, FAKE, FAKE)),
                              FAKE, None, None, 0, FAKE * 16, need, None)
     assert null == INVALID and "experts" in L.moe_last_error().decode()
