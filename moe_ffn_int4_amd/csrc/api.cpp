@@ -650,6 +650,12 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         g.offsets = R.offsets;
         g.counts = R.counts;
         g.tile_base = R.tile_base;
+        // XCD split (time of a routed tile in eighths of a shared bf16 tile,
+        // measured on the Scout and Maverick prefill layers): int4 tiles
+        // dequantize their weights, fp8 256-row tiles run the 128-deep fp8
+        // instruction; in the hybrid path the GEMMs share the chip with the
+        // streaming kernels and equal counts balance best
+        g.routed_weight = hybrid ? 8 : ex4 ? 10 : (ex8 && wide) ? 6 : 8;
 
         g.a = x;
         g.K = d.d;

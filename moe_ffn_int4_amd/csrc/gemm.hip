@@ -15,9 +15,10 @@
 // tokens): row tiles of all groups (tile_base from
 // the dispatch step) x column tiles. Block order is XCD-aware: blocks are
 // dealt round-robin to the 8 XCDs, so each XCD is given a contiguous range of
-// tiles, walked in groups of 8 row tiles x all column tiles; the 64 blocks an
-// XCD runs at a time then share the A and B panels of 8 row tiles x 8 column
-// tiles through that XCD's L2 instead of fetching them from HBM again.
+// tiles (cut by estimated time: xcd_tile), walked in groups of 8 row tiles x
+// all column tiles; the 64 blocks an XCD runs at a time then share the A and
+// B panels of 8 row tiles x 8 column tiles through that XCD's L2 instead of
+// fetching them from HBM again.
 //
 //   up:   H[slot, n]  = silu(A W1^T)[n] * (A W3^T)[n]  (bf16 out)
 //         A = x gathered by slot (routed) or x itself (shared); a block
@@ -428,13 +429,11 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(GroupedGemmArgs a) 
     // ---- block -> (row tile, column tile), XCD-aware (see the file comment)
     const int ncol = static_cast<int>(UP ? a.N / (BN / 2) : (a.N + BN - 1) / BN);
     const int nrow = a.tile_base[a.E + 1];
-    const int total = nrow * ncol;
-    const int L = blockIdx.x;
-    if (L >= total) return;
-    constexpr int kXcd = 8, kGroupRows = 8;
-    const int xcd = L % kXcd, slot = L / kXcd;
-    const int base = total / kXcd, extra = total % kXcd;
-    const int lin = xcd * base + (xcd < extra ? xcd : extra) + slot;  // XCD-contiguous order
+    constexpr int kGroupRows = 8;
+    int lin;
+    if (!xcd_tile(blockIdx.x, static_cast<int64_t>(a.tile_base[a.E]) * ncol, static_cast<int64_t>(nrow) * ncol,
+                  tile_weight(a), lin))
+        return;
     const int span = kGroupRows * ncol;
     const int first_row = (lin / span) * kGroupRows;
     const int rows_here = nrow - first_row < kGroupRows ? nrow - first_row : kGroupRows;
@@ -467,14 +466,14 @@ static hipError_t allow_lds() {
 
 hipError_t launch_grouped_up(const GroupedGemmArgs& a, hipStream_t stream) {
     if (hipError_t e = allow_lds<true>(); e != hipSuccess) return e;
-    dim3 grid(max_row_tiles(a) * static_cast<unsigned>(a.N / (BN / 2)));
+    dim3 grid(xcd_grid(static_cast<int64_t>(max_row_tiles(a)) * (a.N / (BN / 2)), tile_weight(a)));
     hipLaunchKernelGGL(grouped_gemm_kernel<true>, grid, dim3(NT), kGemmLds, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_down(const GroupedGemmArgs& a, hipStream_t stream) {
     if (hipError_t e = allow_lds<false>(); e != hipSuccess) return e;
-    dim3 grid(max_row_tiles(a) * static_cast<unsigned>((a.N + BN - 1) / BN));
+    dim3 grid(xcd_grid(static_cast<int64_t>(max_row_tiles(a)) * ((a.N + BN - 1) / BN), tile_weight(a)));
     hipLaunchKernelGGL(grouped_gemm_kernel<false>, grid, dim3(NT), kGemmLds, stream, a);
     return hipGetLastError();
 }

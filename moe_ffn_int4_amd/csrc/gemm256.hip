@@ -451,19 +451,7 @@ __device__ __forceinline__ void gemm256_tile_fp8(const GroupedGemmArgs& a, const
     }
 }
 
-// Relative time of one routed tile in eighths of a shared-expert (bf16) tile,
-// measured on the Scout prefill layer: int4 tiles dequantize their weights
-// (about 1.27), fp8 tiles run the fp8 instruction at twice the rate (about
-// 0.72), bf16 tiles match the shared expert's.
-__host__ __device__ constexpr int routed_tile_weight(bool f8, bool bf16) { return f8 ? 6 : (bf16 ? 8 : 10); }
-constexpr int kSharedTileWeight = 8;
-
-// XCD-aware block order as in gemm.hip (row tiles of 256 rows), except that
-// each XCD's contiguous range of tiles is cut by estimated time rather than
-// by count: the tile table lists the routed tiles first and the shared
-// expert's after them, and the two kinds differ in cost, so equal counts
-// would leave the XCDs holding the cheaper kind idle at the end. The grid has
-// slots for the largest range an XCD can get; the rest exit at once.
+// XCD-aware block order as in gemm.hip (row tiles of 256 rows; xcd_tile).
 // F8: launches with fp8 routed experts, a separate instantiation so that the
 // int4 / bf16 one keeps its register allocation and schedule.
 template <bool UP, bool F8>
@@ -471,20 +459,11 @@ __global__ __launch_bounds__(NT2, 1) void grouped_gemm256_kernel(GroupedGemmArgs
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int ncol = UP ? static_cast<int>(a.N / (BN2 / 2)) : static_cast<int>((a.N + BN2 - 1) / BN2);
     const int nrow = a.tile_base[a.E + 1];
-    const int L = blockIdx.x;
-    constexpr int kXcd = 8, kGroupRows = 4;
-    const int xcd = L % kXcd, slot = L / kXcd;
-    const int64_t wr = routed_tile_weight(F8, a.wb0 != nullptr);
-    const int64_t routed = static_cast<int64_t>(a.tile_base[a.E]) * ncol;  // tiles
-    const int64_t cr = routed * wr;
-    const int64_t cost = cr + (static_cast<int64_t>(nrow) * ncol - routed) * kSharedTileWeight;
-    // first tile of the XCD whose share of the cost starts at c
-    auto tile_at = [&](int64_t c) {
-        return c <= cr ? (c + wr - 1) / wr : routed + (c - cr + kSharedTileWeight - 1) / kSharedTileWeight;
-    };
-    const int64_t first = tile_at(cost * xcd / kXcd);
-    if (first + slot >= tile_at(cost * (xcd + 1) / kXcd)) return;
-    const int lin = static_cast<int>(first + slot);
+    constexpr int kGroupRows = 4;
+    int lin;
+    if (!xcd_tile(blockIdx.x, static_cast<int64_t>(a.tile_base[a.E]) * ncol, static_cast<int64_t>(nrow) * ncol,
+                  tile_weight(a), lin))
+        return;
     const int span = kGroupRows * ncol;
     const int first_row = (lin / span) * kGroupRows;
     const int rows_here = nrow - first_row < kGroupRows ? nrow - first_row : kGroupRows;
@@ -514,14 +493,7 @@ static hipError_t launch256(const GroupedGemmArgs& a, unsigned ncol, hipStream_t
         reinterpret_cast<const void*>(&grouped_gemm256_kernel<UP, F8>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    // an XCD's share of the cost, at most max_tiles * max weight / 8, in
-    // tiles of the lightest kind, plus one for rounding
-    const int64_t wr = routed_tile_weight(F8, a.wb0 != nullptr);
-    const int64_t wmax = wr > kSharedTileWeight ? wr : kSharedTileWeight;
-    const int64_t wmin = wr < kSharedTileWeight ? wr : kSharedTileWeight;
-    const int64_t tiles = static_cast<int64_t>(max_row_tiles256(a)) * ncol;
-    const int64_t slots = (tiles * wmax + 8 * wmin - 1) / (8 * wmin) + 1;
-    dim3 grid(static_cast<unsigned>(8 * slots));
+    dim3 grid(xcd_grid(static_cast<int64_t>(max_row_tiles256(a)) * ncol, tile_weight(a)));
     hipLaunchKernelGGL((grouped_gemm256_kernel<UP, F8>), grid, dim3(NT2), lds, stream, a);
     return hipGetLastError();
 }

@@ -41,6 +41,43 @@ __device__ __forceinline__ bool find_tile(const GroupedGemmArgs& a, int mt, Tile
     return true;
 }
 
+// Block -> tile position for the grouped GEMMs. Blocks are dealt to the 8
+// XCDs round robin (block L runs on XCD L % 8), and each XCD takes a
+// contiguous range of tile positions, so the tiles it runs at once share A and
+// B panels in its L2. The tile table lists the routed experts' tiles first and
+// the shared expert's after them, and the two kinds differ in cost (int4
+// routed tiles dequantize their weights; fp8 ones run the fp8 instruction), so
+// the ranges are cut by estimated time, not by count: a routed tile weighs
+// `wr`, a shared one kSharedTileWeight. Blocks past their XCD's range return
+// false; the grid has slots for the largest range (xcd_grid).
+constexpr int kSharedTileWeight = 8;
+__host__ __device__ inline int64_t tile_weight(const GroupedGemmArgs& a) {
+    return a.routed_weight > 0 ? a.routed_weight : kSharedTileWeight;
+}
+
+__device__ __forceinline__ bool xcd_tile(int L, int64_t routed, int64_t total, int64_t wr, int& lin) {
+    constexpr int kXcd = 8;
+    const int xcd = L % kXcd, slot = L / kXcd;
+    const int64_t cr = routed * wr;
+    const int64_t cost = cr + (total - routed) * kSharedTileWeight;
+    // first tile of the XCD whose share of the cost starts at c
+    auto tile_at = [&](int64_t c) {
+        return c <= cr ? (c + wr - 1) / wr : routed + (c - cr + kSharedTileWeight - 1) / kSharedTileWeight;
+    };
+    const int64_t first = tile_at(cost * xcd / kXcd);
+    if (first + slot >= tile_at(cost * (xcd + 1) / kXcd)) return false;
+    lin = static_cast<int>(first + slot);
+    return true;
+}
+
+// blocks for at most max_tiles tiles: an XCD's share of the cost is at most
+// max_tiles * max weight / 8, in tiles of the lighter kind, plus one for rounding
+inline unsigned xcd_grid(int64_t max_tiles, int64_t wr) {
+    const int64_t wmax = wr > kSharedTileWeight ? wr : kSharedTileWeight;
+    const int64_t wmin = wr < kSharedTileWeight ? wr : kSharedTileWeight;
+    return static_cast<unsigned>(8 * ((max_tiles * wmax + 8 * wmin - 1) / (8 * wmin) + 1));
+}
+
 // 8 int4 codes (one 32-bit word) times scale -> 4 packed bf16 pairs (RNE)
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -106,6 +106,7 @@ struct GroupedGemmArgs {
     const float* a8s;        //   down: H_q [P, h] by slot) and their row scales
     uint16_t* h_out;         // up: H [P + T, h] bf16
     float* o_out;            // down: O [P + T, d] fp32
+    int routed_weight;       // time of a routed tile in eighths of a shared one (xcd_tile)
 };
 
 // K4 (routed) + K6a (shared): H = silu(A W1^T) * (A W3^T), one launch
