@@ -73,7 +73,8 @@ STAGE_TRAFFIC_KEY = {"decode_up": "decode_up", "grouped_up": "grouped_up"}
 def measured_traffic(stage: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (profiles/traffic.json), or None if there is none for this kernel and
-    workload or the kernel source changed since the counters were taken."""
+    workload or a source file of the kernel or its launch changed since the
+    counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     key = STAGE_TRAFFIC_KEY.get(stage)
@@ -82,9 +83,14 @@ def measured_traffic(stage: str, workload: str):
     rec = json.load(open(path)).get(key)
     if not rec or rec.get("workload") != workload:
         return None
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    # every file that defines the kernel or its launch must be as profiled
+    sources = rec.get("sources_sha256")
+    if not sources:
         return None
+    for rel, digest in sources.items():
+        src = os.path.join(ROOT, rel)
+        if not os.path.isfile(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != digest:
+            return None
     return rec["hbm_bytes_per_launch"]
 
 
