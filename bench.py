@@ -132,9 +132,26 @@ def build_layer(cfg, dev, experts: str = "int4", group: int = 128):
                 routed=experts, group=group)
 
 
-def stage_units(cfg, counts, experts: str = "int4", g: int = 128):
+# the library's AUTO path choice (moe_int4.h): the streaming decode path up to
+# 64 pairs; the hybrid path while the pairs average under 256 per routed
+# expert, whose routed experts with at most 32 pairs stream beside the GEMMs
+DECODE_MAX_PAIRS, HYBRID_AVG_PAIRS, HYBRID_ROWS = 64, 256, 32
+
+
+def resolved_path(cfg, path: str) -> str:
+    P = cfg.T * cfg.top_k
+    if path != "auto":
+        return path
+    if P <= DECODE_MAX_PAIRS:
+        return "decode"
+    return "hybrid" if P < HYBRID_AVG_PAIRS * cfg.E else "prefill_wide"
+
+
+def stage_units(cfg, counts, experts: str = "int4", g: int = 128, path: str = "auto"):
     """Algorithmic bytes and FLOPs of each stage for one launch, given the
-    realized per-expert pair counts of the step (int4: g weights per scale)."""
+    realized per-expert pair counts of the step (int4: g weights per scale).
+    On the hybrid path the GEMM stages count the shared expert and the routed
+    experts with more than HYBRID_ROWS pairs, the streaming stages the rest."""
     T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.top_k
     P = T * k
     touched = int((counts > 0).sum())
@@ -145,19 +162,38 @@ def stage_units(cfg, counts, experts: str = "int4", g: int = 128):
     else:
         w13 = 2 * (h * d // 2 + h * (d // g) * 4)   # one routed expert's W1 + W3 (int4 + scales)
         w2 = d * h // 2 + d * (h // g) * 4          # its W2
-    up_bytes = touched * w13 + 2 * h * d * 2 + T * d * 2 + (P + T) * h * 2
-    down_bytes = touched * w2 + d * h * 2 + (P + T) * h * 2 + (P + T) * d * 4
+
+    def units(n_exp, pairs, shared):
+        """bytes, FLOPs of the up and down launches over n_exp routed experts
+        holding `pairs` pairs, plus the shared expert's T rows if `shared`"""
+        rows = pairs + (T if shared else 0)
+        sw = 2 * h * d * 2 if shared else 0
+        up_b = n_exp * w13 + sw + T * d * 2 + rows * h * 2
+        dn_b = n_exp * w2 + sw // 2 + rows * h * 2 + rows * d * 4
+        return (up_b, 4.0 * rows * d * h), (dn_b, 2.0 * rows * d * h)
+
+    hybrid = resolved_path(cfg, path) == "hybrid"
+    if hybrid:
+        big = counts > HYBRID_ROWS
+        small = (counts > 0) & ~big
+        g_up, g_dn = units(int(big.sum()), int(counts[big].sum()), True)
+        s_up, s_dn = units(int(small.sum()), int(counts[small].sum()), False)
+        gemm_pairs = int(counts[big].sum())
+    else:
+        g_up, g_dn = units(touched, P, True)
+        s_up, s_dn = g_up, g_dn
+        gemm_pairs = P
     return {
         "router": (E * d * 4 + T * d * 2 + T * E * 4, 2.0 * T * d * E),
-        "grouped_up": (up_bytes, 4.0 * (P + T) * d * h),
-        "grouped_down": (down_bytes, 2.0 * (P + T) * d * h),
-        "decode_up": (up_bytes, 4.0 * (P + T) * d * h),
-        "decode_down": (down_bytes + T * d * 2, 2.0 * (P + T) * d * h),
+        "grouped_up": g_up,
+        "grouped_down": g_dn,
+        "decode_up": s_up,
+        "decode_down": (s_dn[0] + T * d * 2, s_dn[1]),
         "combine": ((P + T) * d * 4 + T * d * 2, 2.0 * P * d),
         # fp8 experts: x rows, then H's routed rows, read (bf16) and written (fp8 + scale)
         "act_quant": (T * (d * 3 + 4) + P * (h * 3 + 4), 0.0),
         # FLOPs of the up / down launches on fp8 matrix cores (routed rows), the rest bf16
-        "fp8_flops": {"grouped_up": 4.0 * P * d * h, "grouped_down": 2.0 * P * d * h}
+        "fp8_flops": {"grouped_up": 4.0 * gemm_pairs * d * h, "grouped_down": 2.0 * gemm_pairs * d * h}
         if experts == "fp8" else {},
         "touched": touched,
         "step_bytes": touched * (w13 + w2) + 3 * h * d * 2 + E * d * 4 + 2 * T * d * 2,
@@ -317,7 +353,7 @@ def main() -> int:
     value = cfg0.T * steps / wall
 
     # roofline of the dominant kernel, per launch, averaged over the timed steps
-    units = [stage_units(L["cfg"], c, args.experts, args.group) for L, c in zip(layers, counts)]
+    units = [stage_units(L["cfg"], c, args.experts, args.group, args.path) for L, c in zip(layers, counts)]
     launched = {k: v for k, v in stages.items() if v[1] > 0}
     dom = max(launched, key=lambda k: launched[k][0])
     dom_ms, dom_n = launched[dom]
