@@ -44,9 +44,13 @@ constexpr int NSTAGE2 = 3;
 static_assert(BM2 == 256, "tile table row height");
 }  // namespace
 
-template <bool UP, bool ROUTED>
+// MI: A sub-tiles (16 rows) per wave, 8 for a full 256-row tile; 4 for a half
+// tile of at most 128 rows (the tail of a routed expert), each wave 64 x 128:
+// half the MFMAs, the same B staging.
+template <bool UP, bool ROUTED, int MI = 8>
 __device__ __forceinline__ void gemm256_tile(const GroupedGemmArgs& a, const Tile& tile, int nt,
                                              uint8_t* lds) {
+    static_assert(MI == 8 || MI == 4, "full or half tile");
     const bool routed_rows = tile.group < a.E;
     const int64_t K = a.K, N = a.N;
     const int tid = threadIdx.x;
@@ -56,8 +60,8 @@ __device__ __forceinline__ void gemm256_tile(const GroupedGemmArgs& a, const Til
     const int64_t ng = K / kGroup;
     const int steps = static_cast<int>(K / BK2);
 
-    // ---- A staging: thread -> rows (tid/4) + 64 i (i = 0..3), piece q = tid % 4
-    constexpr int AP = BM2 * BK2 / 8 / NT2;  // 4 pieces per thread
+    // ---- A staging: thread -> rows (tid/4) + 64 i (i < AP), piece q = tid % 4
+    constexpr int AP = MI / 2;  // 4 pieces per thread (256 rows), 2 for a half tile
     const uint16_t* arow[AP];
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
@@ -137,32 +141,32 @@ __device__ __forceinline__ void gemm256_tile(const GroupedGemmArgs& a, const Til
         }
     };
 
-    // ---- fragments: this wave's 8 A sub-tiles (rows wm*128 ..) and 8 B sub-tiles
+    // ---- fragments: this wave's MI A sub-tiles (rows wm*16*MI ..) and 8 B sub-tiles
     const int lslot = frag_slot(lane & 15, lane >> 4);
-    int a_off[8], b_off[8];
+    int a_off[MI], b_off[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a_off[i] = (wm * 8 + i) * SUB2 + lslot;
+    for (int i = 0; i < MI; ++i) a_off[i] = (wm * MI + i) * SUB2 + lslot;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         b_off[j] = ASUB2 * SUB2 + lslot +
                    SUB2 * (UP ? ((j < 4) ? wn * 4 + j : 8 + wn * 4 + (j - 4)) : wn * 8 + j);
 
-    bf16x8 fa0[8], fb0[8], fa1[8], fb1[8];
-    auto read_frags = [&](bf16x8 (&fa)[8], bf16x8 (&fb)[8], int stage) __attribute__((always_inline)) {
+    bf16x8 fa0[MI], fb0[8], fa1[MI], fb1[8];
+    auto read_frags = [&](bf16x8 (&fa)[MI], bf16x8 (&fb)[8], int stage) __attribute__((always_inline)) {
         const uint8_t* st = lds + stage * STAGE2;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             fb[i] = *reinterpret_cast<const bf16x8*>(st + b_off[i]);
-            fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i]);
+            if (i < MI) fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i]);
         }
     };
 
-    f32x4 acc[8][8];
-    auto mfma_step = [&](const bf16x8 (&fa)[8], const bf16x8 (&fb)[8], auto first)
+    f32x4 acc[MI][8];
+    auto mfma_step = [&](const bf16x8 (&fa)[MI], const bf16x8 (&fb)[8], auto first)
                          __attribute__((always_inline)) {
         constexpr bool FIRST = decltype(first)::value;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -177,7 +181,7 @@ __device__ __forceinline__ void gemm256_tile(const GroupedGemmArgs& a, const Til
     // dequantized 8-code word of B), alternating A and B pieces so that the
     // dequantization spreads over the chunks; each register of the staging set
     // is requested again as soon as it has been stored.
-    auto step = [&](const bf16x8 (&fa)[8], const bf16x8 (&fb)[8], bf16x8 (&na)[8], bf16x8 (&nb)[8],
+    auto step = [&](const bf16x8 (&fa)[MI], const bf16x8 (&fb)[8], bf16x8 (&na)[MI], bf16x8 (&nb)[8],
                     u32x4 (&ra)[AP], u32x4 (&rb)[BV], float& rs, int k, int rd, int wr, auto first)
                     __attribute__((always_inline)) {
         constexpr bool FIRST = decltype(first)::value;
@@ -189,16 +193,23 @@ __device__ __forceinline__ void gemm256_tile(const GroupedGemmArgs& a, const Til
         const int qn = kn & 3;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+            // chunk i: A sub-tile i against all 8 B fragments (full tile), or
+            // A sub-tile i / 2 against B fragments 4 (i % 2) .. + 3 (half tile)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    fa[i], fb[j], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i][j], 0, 0, 0);
+            for (int jj = 0; jj < MI; ++jj) {
+                const int ai = MI == 8 ? i : i >> 1;
+                const int j = MI == 8 ? jj : 4 * (i & 1) + jj;
+                acc[ai][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    fa[ai], fb[j], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[ai][j], 0, 0, 0);
+            }
             nb[i] = *reinterpret_cast<const bf16x8*>(rs_st + b_off[i]);
-            na[i] = *reinterpret_cast<const bf16x8*>(rs_st + a_off[i]);
+            if (i < MI) na[i] = *reinterpret_cast<const bf16x8*>(rs_st + a_off[i]);
             const int piece = i >> 1;
             if ((i & 1) == 0) {
-                *reinterpret_cast<u32x4*>(ws_st + a_st + 4 * piece * SUB2) = ra[piece];
-                ra[piece] = *reinterpret_cast<const u32x4*>(arow[piece] + kn0);
+                if (piece < AP) {
+                    *reinterpret_cast<u32x4*>(ws_st + a_st + 4 * piece * SUB2) = ra[piece];
+                    ra[piece] = *reinterpret_cast<const u32x4*>(arow[piece] + kn0);
+                }
             } else {
                 if (ROUTED) {
                     *reinterpret_cast<u32x4*>(ws_st + b_st + frag_slot(tid & 15, piece)) =
@@ -216,16 +227,16 @@ __device__ __forceinline__ void gemm256_tile(const GroupedGemmArgs& a, const Til
             // MFMAs paced with the chunk's other work
             if (ROUTED && (i & 1)) {
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
+                for (int t = 0; t < MI; ++t) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 32 / MI, 0);
                 }
             } else {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, MI / 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, MI / 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, MI / 2, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -262,10 +273,10 @@ __device__ __forceinline__ void gemm256_tile(const GroupedGemmArgs& a, const Til
     // ---- epilogue: D[row][col], row = 4 * lq + r inside a 16 x 16 sub-tile, col = l16
     const int l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = wm * 128 + i * 16 + lq * 4 + r;
+            const int row = wm * 16 * MI + i * 16 + lq * 4 + r;
             if (row >= tile.nrows) continue;
             const int64_t orow = tile.row0 + row;
             if (UP) {
@@ -473,6 +484,7 @@ __global__ __launch_bounds__(NT2, 1) void grouped_gemm256_kernel(GroupedGemmArgs
     Tile tile;
     if (!find_tile<BM2>(a, mt, tile)) return;
     if (F8 && tile.group < a.E) gemm256_tile_fp8<UP>(a, tile, nt, lds);
+    else if (!F8 && tile.group < a.E && !a.wb0 && tile.nrows <= 128) gemm256_tile<UP, true, 4>(a, tile, nt, lds);
     else if (!F8 && tile.group < a.E && !a.wb0) gemm256_tile<UP, true>(a, tile, nt, lds);
     else gemm256_tile<UP, false>(a, tile, nt, lds);
 }
