@@ -312,11 +312,42 @@ __device__ __forceinline__ void compute_fp8(const Fp8Slot& sl, f32x4& acc0, f32x
     }
 }
 
+// Sliced A staging for routed chunks of more rows than fit whole in LDS: a
+// slice is half a round of the LDS path's weight ring ((DL + 1) / 2 groups;
+// a whole round when DL + 1 is odd). Two slices of 16 rows then fit the LDS
+// the kernel already takes (25 KB up, 33.3 KB down at groups of 128), and the
+// staging registers stay within the up projection's three waves per SIMD.
+constexpr int slice_groups(bool up, int dl) { return (dl + 1) % 2 == 0 ? (dl + 1) / 2 : dl + 1; }
+constexpr size_t slice_lds_bytes(int sg) { return 2 * size_t(kDecodeRows) * (sg * kGroup + 8) * 2; }
+
+// slice j of the chunk's A rows into registers: this thread's PP 16-byte pieces
+// (source row start, column in the slice); past the last slice, the last
+// slice again; columns past K (a partial last slice) re-read column K - 8
+template <int PP, int SG>
+__device__ __forceinline__ void slice_load(uint4 (&pv)[PP], const uint16_t* const (&psrc)[PP],
+                                           const int (&pcol)[PP], int j, int nsl, int64_t K) {
+    j = j < nsl ? j : nsl - 1;
+    const int64_t c0 = static_cast<int64_t>(j) * SG * kGroup;
+#pragma unroll
+    for (int p = 0; p < PP; ++p) {
+        const int64_t col = c0 + pcol[p] < K ? c0 + pcol[p] : K - 8;
+        pv[p] = *reinterpret_cast<const uint4*>(psrc[p] + col);
+    }
+}
+
+template <int PP>
+__device__ __forceinline__ void slice_store(const uint4 (&pv)[PP], const int (&pdst)[PP], uint16_t* buf) {
+#pragma unroll
+    for (int p = 0; p < PP; ++p) *reinterpret_cast<uint4*>(buf + pdst[p]) = pv[p];
+}
+
 // DR / DS: groups kept in flight ahead of the one being computed, for int4
 // (routed) and bf16 (shared) weights
 // F8: the routed experts are fp8 (a separate instantiation, so the int4 one
 // keeps its register budget); S: int4 scales per 128-column tile row
-template <bool UP, int DR, int DS, int DL, bool F8, int S>
+// SL: int4 chunks of more rows than fit whole in LDS stage A in slices (groups
+// of 128; chosen by the host for batches averaging 4+ pairs per expert)
+template <bool UP, int DR, int DS, int DL, bool F8, int S, bool SL>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     // routed chunks of at most a.lds_rows rows keep their A rows in LDS
     extern __shared__ __attribute__((aligned(16))) uint16_t a_lds[];
@@ -436,7 +467,91 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < D; ++u)
             if (u < ng - full) compute_lds<UP, S>(sl[u], lrow, full + u, acc0, acc1);
+    } else if (int4 && SL) {
+        // Chunks of more than lds_rows rows: the block stages A in slices of SG
+        // groups (SG * 128 columns of the chunk's rows). Two slices sit in LDS:
+        // slice j+1 goes from registers into the other buffer at the end of
+        // slice j, one barrier per slice, and slice j+2 is then requested. The
+        // weight ring is the LDS path's, and slices end at fixed ring
+        // positions. (Each wave reading its A rows from L2 for its own 16
+        // features moved rows / 4 times the weight bytes per wave.)
+        constexpr int D = DL;
+        constexpr int U = D + 1;
+        constexpr int SG = slice_groups(UP, DL);
+        static_assert(U % SG == 0, "slices end at fixed ring positions");
+        constexpr int SW = SG * kGroup + 8;                // row pitch of a slice (16-byte pad)
+        constexpr int PP = kDecodeRows * SG * 16 / NT;    // 16-byte pieces per thread per slice
+        static_assert(PP * NT == kDecodeRows * SG * 16, "whole pieces per thread");
+        const int64_t rb = static_cast<int64_t>(group) * (N / 16) + (n >> 4);
+        const uint8_t* q0 = a.wq0 + rb * ng * 1024 + kq * 256 + l16 * 16;
+        const uint8_t* q1 = UP ? a.wq1 + rb * ng * 1024 + kq * 256 + l16 * 16 : nullptr;
+        const float* s0 = a.ws0 + (rb * ng * 16 + l16) * S;
+        const float* s1 = UP ? a.ws1 + (rb * ng * 16 + l16) * S : nullptr;
+        WeightSlot<S> sl[U];
+#pragma unroll
+        for (int p = 0; p < D; ++p) load_weights<UP, S>(sl[p], q0, q1, s0, s1, min(p, ng - 1));
+        // piece tid + NT p of a slice: row pc / (16 SG), columns 8 (pc % (16 SG)) ..;
+        // rows past the chunk repeat its last row (never read)
+        const uint16_t* psrc[PP];
+        int pcol[PP], pdst[PP];
+#pragma unroll
+        for (int p = 0; p < PP; ++p) {
+            const int pc = tid + NT * p;
+            const int r = pc / (SG * 16);
+            pcol[p] = (pc % (SG * 16)) * 8;
+            const int rr = r < nrows ? r : nrows - 1;
+            const int64_t srow = UP ? a.perm[row0 + rr] / a.top_k : row0 + rr;
+            psrc[p] = a.a_perm + srow * K;
+            pdst[p] = r * SW + pcol[p];
+        }
+        const int nsl = (ng + SG - 1) / SG;
+        uint4 pv[PP];
+        uint16_t* const buf0 = a_lds;
+        uint16_t* const buf1 = a_lds + kDecodeRows * SW;
+        slice_load<PP, SG>(pv, psrc, pcol, 0, nsl, K);
+        slice_store<PP>(pv, pdst, buf0);
+        __syncthreads();
+        const uint16_t* lbase = a_lds + m * SW + (S == 1 ? kq * 32 : kq * 8);
+        // Slice s sits in buffer s % 2. A slice's first group requests the next
+        // slice into registers; its last group stores it into the other buffer
+        // (whose previous slice was last read before the previous barrier), then
+        // a barrier. Rounds of U groups hold whole slices, so nothing is carried
+        // in registers from one round to the next.
+        const int full = ng - ng % U;
+        for (int g0 = 0; g0 < full; g0 += U) {
+            const int j0 = g0 / SG;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = j0 + u / SG;
+                if (u % SG == 0) slice_load<PP, SG>(pv, psrc, pcol, j + 1, nsl, K);
+                load_weights<UP, S>(sl[(u + D) % U], q0, q1, s0, s1, min(g0 + u + D, ng - 1));
+                compute_lds<UP, S>(sl[u], lbase + (j & 1) * (kDecodeRows * SW), u % SG, acc0, acc1);
+                if ((u + 1) % SG == 0) {
+                    slice_store<PP>(pv, pdst, (j & 1) ? buf0 : buf1);
+                    __syncthreads();
+                }
+            }
+        }
+        // the last ng % U groups (already in the ring): their first slice is in
+        // LDS; a later one (only when a slice is shorter than a round) is staged
+        // on the spot
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            if (u < ng - full) {
+                const int g = full + u;
+                const int j = g / SG;
+                if (u > 0 && g % SG == 0) {
+                    slice_load<PP, SG>(pv, psrc, pcol, j, nsl, K);
+                    slice_store<PP>(pv, pdst, (j & 1) ? buf1 : buf0);
+                    __syncthreads();
+                }
+                compute_lds<UP, S>(sl[u], lbase + (j & 1) * (kDecodeRows * SW), g % SG, acc0, acc1);
+            }
+        }
     } else if (int4) {
+        // each wave reads its A rows from L2 with its weights (few rows per chunk,
+        // or groups of 64 / 32, where the sliced staging's registers would cost
+        // a wave per SIMD)
         constexpr int D = DR;
         constexpr int U = D + 1;
         // tile row block of this lane's feature; tiles of a row block are consecutive
@@ -540,7 +655,7 @@ static int lds_rows(int64_t K) {
 // max_chunks bounds the chunk list, shared_chunks is the number of shared-expert
 // chunks at its head (0 when the shared expert runs on the GEMMs)
 // F8 / S pick the kernel instantiation (fp8 experts, int4 scales per tile row)
-template <bool UP, int DR, int DS, int DL, bool F8, int S>
+template <bool UP, int DR, int DS, int DL, bool F8, int S, bool SL = false>
 static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, int shared_chunks,
                                 hipStream_t stream) {
     DecodeArgs a = args;
@@ -548,8 +663,12 @@ static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, int shar
     a.max_chunks = max_chunks;
     size_t lds = a.lds_rows > 0 ? static_cast<size_t>(a.lds_rows) * (a.K + 8) * 2 : 0;
     lds = lds > kReduceLdsBytes ? lds : kReduceLdsBytes;
+    // int4 chunks past lds_rows rows stage A in slices (SL)
+    static_assert(!SL || (S == 1 && !F8), "sliced staging: int4 groups of 128");
+    constexpr size_t sliced = SL ? slice_lds_bytes(slice_groups(UP, DL)) : 0;
+    if (a.lds_rows < kDecodeRows && lds < sliced) lds = sliced;
     dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks + 3 * shared_chunks));
-    hipLaunchKernelGGL((decode_kernel<UP, DR, DS, DL, F8, S>), grid, dim3(NT), lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<UP, DR, DS, DL, F8, S, SL>), grid, dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -563,6 +682,7 @@ hipError_t launch_decode_up(const DecodeArgs& args, int max_chunks, int shared_c
     if (args.wf0) return launch_decode<true, 3, 1, 7, true, 1>(args, max_chunks, shared_chunks, stream);
     if (args.spt == 2) return launch_decode<true, 3, 1, 5, false, 2>(args, max_chunks, shared_chunks, stream);
     if (args.spt == 4) return launch_decode<true, 2, 1, 4, false, 4>(args, max_chunks, shared_chunks, stream);
+    if (args.sliced) return launch_decode<true, 3, 1, 5, false, 1, true>(args, max_chunks, shared_chunks, stream);
     return launch_decode<true, 3, 1, 5, false, 1>(args, max_chunks, shared_chunks, stream);
 }
 
@@ -571,6 +691,7 @@ hipError_t launch_decode_down(const DecodeArgs& args, int max_chunks, int shared
     if (args.wf0) return launch_decode<false, 3, 2, 7, true, 1>(args, max_chunks, shared_chunks, stream);
     if (args.spt == 2) return launch_decode<false, 3, 2, 7, false, 2>(args, max_chunks, shared_chunks, stream);
     if (args.spt == 4) return launch_decode<false, 2, 2, 5, false, 4>(args, max_chunks, shared_chunks, stream);
+    if (args.sliced) return launch_decode<false, 3, 2, 7, false, 1, true>(args, max_chunks, shared_chunks, stream);
     return launch_decode<false, 3, 2, 7, false, 1>(args, max_chunks, shared_chunks, stream);
 }
 

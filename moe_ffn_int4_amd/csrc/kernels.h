@@ -147,6 +147,7 @@ struct DecodeArgs {
     const float* a8s;
     uint16_t* h_out;
     float* o_out;
+    int sliced;              // int4 groups of 128: larger chunks stage A in LDS slices
     int lds_rows;            // set by the launcher: routed chunks this small stage A in LDS
     int max_chunks;          // set by the launcher: grid rows of the chunk list
 };

@@ -69,6 +69,31 @@ def test_small_layers_every_token(name, path):
     _check(layer, y, ids, np.arange(cfg.T))
 
 
+# Streaming chunks of more rows than fit whole in LDS at these K (up to 16
+# rows against 7..15 that fit): the chunk's A rows go through LDS in slices.
+# Cases: whole ring rounds only; a one-group tail in a partial last slice; a
+# tail spanning two slices (both projections); top-2. Groups of 64 keep each
+# wave reading its A rows from L2.
+SLICED = {
+    "rounds only": W.config(0).with_(T=48, d=1536, E=3, h=3072, top_k=1),
+    "one-group tail": W.config(0).with_(T=48, d=1664, E=3, h=3200, top_k=1),
+    "tail over two slices": W.config(0).with_(T=40, d=2048, E=2, h=1664, top_k=1),
+    "top-2": W.config(0).with_(T=40, d=2048, E=4, h=1664, top_k=2),
+}
+
+
+@pytest.mark.parametrize("group", [128, 64])
+@pytest.mark.parametrize("name", list(SLICED))
+def test_decode_chunks_past_lds_rows(name, group):
+    cfg = SLICED[name]
+    say(f"forward[decode]: {name} T={cfg.T} d={cfg.d} E={cfg.E} h={cfg.h} k={cfg.top_k} g={group}")
+    layer = build_layer(cfg, group=group)
+    y, ids, _ = _run(layer, "decode")
+    counts = np.bincount(ids.ravel(), minlength=cfg.E)
+    assert counts.max() >= 16, counts  # at least one full 16-row chunk
+    _check(layer, y, ids, np.arange(cfg.T))
+
+
 def test_tiny_layer_all_paths_agree():
     layer = build_layer(W.config(0))
     y1, i1, _ = _run(layer, "prefill")
