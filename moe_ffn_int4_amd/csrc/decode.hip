@@ -12,7 +12,9 @@
 // For int4 and fp8 experts each wave owns 16 output features and streams them
 // over the whole reduction dimension on its own, keeping the next tiles'
 // loads in flight in a register ring; chunks of a few rows first stage their
-// A rows in LDS once per block. bf16 chunks (the shared expert, bf16 experts)
+// A rows in LDS once per block, and larger int4 chunks stage them in LDS
+// slices along the reduction (the SL instantiation, chosen by the host for
+// batches averaging 4+ pairs per expert). bf16 chunks (the shared expert, bf16 experts)
 // carry four times the bytes of int4: four blocks share a 64-feature range,
 // each wave of a block streams a quarter of the reduction, and the four
 // partial sums are added in LDS in wave order. v_mfma_f32_16x16x32_bf16 takes

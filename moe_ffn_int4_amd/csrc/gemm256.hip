@@ -24,8 +24,11 @@
 // retires the reads of step k+1's stage before step k+2 (the next writer of
 // that stage is step k+3's data, stored in iteration k+1... after that barrier).
 //
-// Partial row tiles run all MFMAs on clamped rows (results dropped). Tiles of
-// fp8 experts run their own body (gemm256_tile_fp8).
+// Partial row tiles run all MFMAs on clamped rows (results dropped); a routed
+// int4 tile of at most 128 rows (an expert's tail) runs a half-height body
+// (each wave 64 x 128). Tiles of fp8 experts run their own body on the 128-deep
+// fp8 instruction (gemm256_tile_fp8). Blocks map to tiles by xcd_tile: each
+// XCD takes a contiguous range of tiles cut by estimated time.
 #include <type_traits>
 
 #include "gemm_common.h"
