@@ -297,10 +297,14 @@ def main() -> int:
         moe.forward(L["x"], L["wr"], L["b"], L["experts"], L["shared"], cfg0.top_k,
                     path=args.path, y=y, topk_ids=ids[i % nlayers], workspace=ws)
 
+    # each layer copy's per-expert pair counts (for the algorithmic bytes and
+    # FLOPs of its launches), from the library's routing call, so they do not
+    # depend on which copies the warmup steps reached
+    counts = [moe.route(L["x"], L["wr"], L["b"], cfg0.top_k)["counts"].cpu().numpy().astype(np.int64)
+              for L in layers]
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    counts = [np.bincount(t.cpu().numpy().ravel(), minlength=cfg0.E) for t in ids]
     print(f"[bench] warmup done; experts touched per layer copy: "
           f"{[int((c > 0).sum()) for c in counts]}", file=sys.stderr, flush=True)
 
