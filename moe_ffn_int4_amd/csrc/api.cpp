@@ -19,6 +19,13 @@
 static_assert(MOE_MAX_EXPERTS == moe::kMaxExperts, "expert limit mismatch");
 static_assert(MOE_GROUP_SIZE == moe::kGroup, "group size mismatch");
 
+namespace moe {
+LaunchTiming& launch_timing() {
+    static thread_local LaunchTiming t;
+    return t;
+}
+}  // namespace moe
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -176,7 +183,8 @@ hipError_t prof_event(hipEvent_t* ev) {
     return hipEventCreate(ev);
 }
 
-// Launch `fn` (returning hipError_t) as `stage`, bracketed by events when enabled.
+// Launch `fn` (returning hipError_t) as `stage`; when timing is enabled its
+// kernels record a pair of events at the first one's start and the last one's end.
 template <typename F>
 int timed(int stage, hipStream_t s, const char* what, F&& fn) {
     Prof& P = prof();
@@ -189,10 +197,21 @@ int timed(int stage, hipStream_t s, const char* what, F&& fn) {
     Prof::Rec r{stage, nullptr, nullptr};
     HIP_CHECK(prof_event(&r.a), "hipEventCreate");
     HIP_CHECK(prof_event(&r.b), "hipEventCreate");
-    HIP_CHECK(hipEventRecord(r.a, s), "hipEventRecord");
-    HIP_CHECK(fn(), what);
-    HIP_CHECK(hipEventRecord(r.b, s), "hipEventRecord");
-    P.pending.push_back(r);
+    // the stage's kernels record the events at their own start and end
+    moe::LaunchTiming& lt = moe::launch_timing();
+    lt.start = r.a;
+    lt.stop = r.b;
+    const hipError_t e = fn();
+    const bool launched = lt.start == nullptr;  // the first launch took the start event
+    lt.start = lt.stop = nullptr;
+    if (launched) {
+        P.pending.push_back(r);
+    } else {
+        P.pool.push_back(r.a);
+        P.pool.push_back(r.b);
+    }
+    HIP_CHECK(e, what);
+    (void)s;
     return MOE_OK;
 }
 

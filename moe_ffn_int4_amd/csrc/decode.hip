@@ -670,7 +670,7 @@ static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, int shar
     constexpr size_t sliced = SL ? slice_lds_bytes(slice_groups(UP, DL)) : 0;
     if (a.lds_rows < kDecodeRows && lds < sliced) lds = sliced;
     dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks + 3 * shared_chunks));
-    hipLaunchKernelGGL((decode_kernel<UP, DR, DS, DL, F8, S, SL>), grid, dim3(NT), lds, stream, a);
+    MOE_LAUNCH((decode_kernel<UP, DR, DS, DL, F8, S, SL>), grid, dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
 

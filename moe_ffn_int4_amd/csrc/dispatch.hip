@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
 hipError_t launch_dispatch(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_rows,
                            int small_rows, int32_t* counts, int32_t* offsets, int32_t* tile_base, int32_t* perm,
                            int32_t* inv, int4* chunks, int32_t* nchunks, hipStream_t stream) {
-    hipLaunchKernelGGL(dispatch_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, stream, ids,
+    MOE_LAUNCH(dispatch_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, stream, ids,
                        T, top_k, static_cast<int>(E), tile_rows, small_rows, counts, offsets, tile_base, perm,
                        inv, chunks, nchunks);
     return hipGetLastError();

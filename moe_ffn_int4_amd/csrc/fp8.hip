@@ -85,7 +85,7 @@ __global__ __launch_bounds__(NT) void quantize_fp8_rows_kernel(const SRC* __rest
 hipError_t launch_quantize_fp8_weights(const float* w, int64_t rows, int64_t K, uint8_t* q,
                                        float* scales, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL((quantize_fp8_rows_kernel<float, true>), dim3(static_cast<unsigned>(rows)),
+    MOE_LAUNCH((quantize_fp8_rows_kernel<float, true>), dim3(static_cast<unsigned>(rows)),
                        dim3(NT), 0, stream, w, K, 0.f, q, scales);
     return hipGetLastError();
 }
@@ -93,7 +93,7 @@ hipError_t launch_quantize_fp8_weights(const float* w, int64_t rows, int64_t K, 
 hipError_t launch_quantize_fp8_activations(const uint16_t* x, int64_t rows, int64_t K, float ub,
                                            uint8_t* q, float* scales, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL((quantize_fp8_rows_kernel<uint16_t, false>), dim3(static_cast<unsigned>(rows)),
+    MOE_LAUNCH((quantize_fp8_rows_kernel<uint16_t, false>), dim3(static_cast<unsigned>(rows)),
                        dim3(NT), 0, stream, x, K, ub, q, scales);
     return hipGetLastError();
 }

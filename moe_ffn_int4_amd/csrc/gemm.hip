@@ -467,14 +467,14 @@ static hipError_t allow_lds() {
 hipError_t launch_grouped_up(const GroupedGemmArgs& a, hipStream_t stream) {
     if (hipError_t e = allow_lds<true>(); e != hipSuccess) return e;
     dim3 grid(xcd_grid(static_cast<int64_t>(max_row_tiles(a)) * (a.N / (BN / 2)), tile_weight(a)));
-    hipLaunchKernelGGL(grouped_gemm_kernel<true>, grid, dim3(NT), kGemmLds, stream, a);
+    MOE_LAUNCH(grouped_gemm_kernel<true>, grid, dim3(NT), kGemmLds, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_down(const GroupedGemmArgs& a, hipStream_t stream) {
     if (hipError_t e = allow_lds<false>(); e != hipSuccess) return e;
     dim3 grid(xcd_grid(static_cast<int64_t>(max_row_tiles(a)) * ((a.N + BN - 1) / BN), tile_weight(a)));
-    hipLaunchKernelGGL(grouped_gemm_kernel<false>, grid, dim3(NT), kGemmLds, stream, a);
+    MOE_LAUNCH(grouped_gemm_kernel<false>, grid, dim3(NT), kGemmLds, stream, a);
     return hipGetLastError();
 }
 
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_combine(const float* O, const float* gates, const int32_t* inv, int64_t T,
                           int64_t P, int top_k, int64_t d, uint16_t* y, hipStream_t stream) {
     const int64_t n = T * (d / 4);
-    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+    MOE_LAUNCH(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                        stream, O, gates, inv, T, P, top_k, d, y);
     return hipGetLastError();
 }

@@ -509,7 +509,7 @@ static hipError_t launch256(const GroupedGemmArgs& a, unsigned ncol, hipStream_t
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     dim3 grid(xcd_grid(static_cast<int64_t>(max_row_tiles256(a)) * ncol, tile_weight(a)));
-    hipLaunchKernelGGL((grouped_gemm256_kernel<UP, F8>), grid, dim3(NT2), lds, stream, a);
+    MOE_LAUNCH((grouped_gemm256_kernel<UP, F8>), grid, dim3(NT2), lds, stream, a);
     return hipGetLastError();
 }
 

@@ -1,10 +1,35 @@
 // kernels.h -- host-side launchers of the gfx950 kernels (internal to the library).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Per-stage kernel timing (moe_profile_*). While the host has set `stop`, each
+// launch of this thread goes through hipExtLaunchKernelGGL, which records the
+// events at the kernel's own start and end: the stage's first launch takes
+// `start` (then cleared), every launch records `stop`. Otherwise launches are
+// plain hipLaunchKernelGGL.
+struct LaunchTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+LaunchTiming& launch_timing();
+
+#define MOE_LAUNCH(kernel, grid, block, lds, stream, ...)                                     \
+    do {                                                                                      \
+        ::moe::LaunchTiming& lt_ = ::moe::launch_timing();                                    \
+        if (lt_.stop) {                                                                       \
+            hipEvent_t st_ = lt_.start;                                                       \
+            lt_.start = nullptr;                                                              \
+            hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), stream, st_, \
+                                  lt_.stop, 0, __VA_ARGS__);                                  \
+        } else {                                                                              \
+            hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                \
+        }                                                                                     \
+    } while (0)
 
 // Tile width of the tiled weight layouts (columns per 16-row tile), and the
 // default quantization group. Int4 groups of 64 or 32 weights keep the same

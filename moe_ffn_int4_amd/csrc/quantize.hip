@@ -80,11 +80,11 @@ hipError_t launch_quantize_int4(const float* w, int64_t rows, int64_t K, int gro
     const int64_t want = (ngroups + 7) / 8;  // 8 units per 256-thread block per pass
     const int blocks = static_cast<int>(want < 8192 ? want : 8192);
     if (tiled)
-        hipLaunchKernelGGL(quantize_int4_kernel<true>, dim3(blocks), dim3(256), 0, stream,
+        MOE_LAUNCH(quantize_int4_kernel<true>, dim3(blocks), dim3(256), 0, stream,
                            reinterpret_cast<const float4*>(w), ngroups, K / kGroup, group,
                            reinterpret_cast<uint16_t*>(q), scales);
     else
-        hipLaunchKernelGGL(quantize_int4_kernel<false>, dim3(blocks), dim3(256), 0, stream,
+        MOE_LAUNCH(quantize_int4_kernel<false>, dim3(blocks), dim3(256), 0, stream,
                            reinterpret_cast<const float4*>(w), ngroups, K / kGroup, group,
                            reinterpret_cast<uint16_t*>(q), scales);
     return hipGetLastError();
@@ -113,7 +113,7 @@ hipError_t launch_pack_bf16(const uint16_t* src, int64_t rows, int64_t K, uint16
     if (n16 == 0) return hipSuccess;
     const int64_t want = (n16 + 255) / 256;
     const int blocks = static_cast<int>(want < 16384 ? want : 16384);
-    hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, stream,
+    MOE_LAUNCH(pack_bf16_kernel, dim3(blocks), dim3(256), 0, stream,
                        reinterpret_cast<const uint4*>(src), K, n16, reinterpret_cast<uint4*>(dst));
     return hipGetLastError();
 }

@@ -293,18 +293,18 @@ hipError_t launch_router_partials(const uint16_t* x, const float* wr, int64_t T,
     if (p.kind == 4) {
         const int64_t n = E * d;
         const int64_t want = (n + 255) / 256;
-        hipLaunchKernelGGL(router_split_kernel, dim3(static_cast<unsigned>(want < 4096 ? want : 4096)),
+        MOE_LAUNCH(router_split_kernel, dim3(static_cast<unsigned>(want < 4096 ? want : 4096)),
                            dim3(256), 0, stream, wr, n, wparts);
         const int64_t slice = d / p.slices;
         if (E <= 16) {
             const int64_t tasks = (T + 31) / 32;
-            hipLaunchKernelGGL((router_mfma_kernel<1>),
+            MOE_LAUNCH((router_mfma_kernel<1>),
                                dim3(static_cast<unsigned>((tasks + 3) / 4), static_cast<unsigned>(p.slices)),
                                dim3(256), 0, stream, x, wparts, T, d, E, 1, slice, partials, x_perm);
         } else {
             const int n_et = static_cast<int>((E + 31) / 32);
             const int64_t tasks = ((T + 31) / 32) * n_et;
-            hipLaunchKernelGGL((router_mfma_kernel<2>),
+            MOE_LAUNCH((router_mfma_kernel<2>),
                                dim3(static_cast<unsigned>((tasks + 3) / 4), static_cast<unsigned>(p.slices)),
                                dim3(256), 0, stream, x, wparts, T, d, E, n_et, slice, partials, x_perm);
         }
@@ -315,19 +315,19 @@ hipError_t launch_router_partials(const uint16_t* x, const float* wr, int64_t T,
     const int64_t slice = d / p.slices;
     switch (p.kind) {
         case 0:
-            hipLaunchKernelGGL((router_partials_kernel<16, 16, 1, 1>), grid, dim3(256), 0, stream, x,
+            MOE_LAUNCH((router_partials_kernel<16, 16, 1, 1>), grid, dim3(256), 0, stream, x,
                                wr, T, d, E, slice, partials, x_perm);
             break;
         case 1:
-            hipLaunchKernelGGL((router_partials_kernel<128, 16, 8, 1>), grid, dim3(256), 0, stream, x,
+            MOE_LAUNCH((router_partials_kernel<128, 16, 8, 1>), grid, dim3(256), 0, stream, x,
                                wr, T, d, E, slice, partials, x_perm);
             break;
         case 2:
-            hipLaunchKernelGGL((router_partials_kernel<64, 32, 4, 2>), grid, dim3(256), 0, stream, x,
+            MOE_LAUNCH((router_partials_kernel<64, 32, 4, 2>), grid, dim3(256), 0, stream, x,
                                wr, T, d, E, slice, partials, x_perm);
             break;
         default:
-            hipLaunchKernelGGL((router_partials_kernel<32, 64, 2, 4>), grid, dim3(256), 0, stream, x,
+            MOE_LAUNCH((router_partials_kernel<32, 64, 2, 4>), grid, dim3(256), 0, stream, x,
                                wr, T, d, E, slice, partials, x_perm);
             break;
     }
@@ -433,7 +433,7 @@ hipError_t launch_topk(const float* partials, int slices, const float* bias, int
                        int top_k, float* logits, int32_t* ids, float* gates, int32_t* ids_copy,
                        float* gates_copy, hipStream_t stream) {
     const unsigned blocks = static_cast<unsigned>((T + 3) / 4);  // 4 waves (tokens) per block
-    hipLaunchKernelGGL(topk_kernel, dim3(blocks), dim3(256), 0, stream, partials, slices, bias, T, E,
+    MOE_LAUNCH(topk_kernel, dim3(blocks), dim3(256), 0, stream, partials, slices, bias, T, E,
                        top_k, logits, ids, gates, ids_copy, gates_copy);
     return hipGetLastError();
 }
@@ -591,7 +591,7 @@ hipError_t launch_route_small(const float* partials, int slices, const float* bi
                               int32_t* ids, float* gates, int32_t* ids_copy, float* gates_copy,
                               int32_t* counts, int32_t* offsets, int32_t* tile_base, int32_t* perm,
                               int32_t* inv, int4* chunks, int32_t* nchunks, hipStream_t stream) {
-    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(1024), 0, stream, partials, slices, bias, T,
+    MOE_LAUNCH(route_small_kernel, dim3(1), dim3(1024), 0, stream, partials, slices, bias, T,
                        static_cast<int>(E), top_k, tile_rows, small_rows, logits, ids, gates, ids_copy,
                        gates_copy, counts, offsets, tile_base, perm, inv, chunks, nchunks);
     return hipGetLastError();
