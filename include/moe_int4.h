@@ -275,12 +275,15 @@ int moe_route(const moe_dims *dims, const uint16_t *x, const float *router_w,
 
 /*
  * Per-stage timing for benchmarks (not part of the layer's arithmetic).
- * While enabled, every moe_forward / moe_route call records a hipEvent on its
- * stream before and after each kernel launch. moe_profile_read waits for the
- * recorded events, writes the summed duration in milliseconds and the launch
- * count of each stage (arrays of `n` entries, n <= MOE_STAGE_COUNT), and
- * resets the sums. Enabling adds one event record per launch; it is off by
- * default. State is process-wide; it is not meant for concurrent callers.
+ * While enabled, each stage of every moe_forward / moe_route call is timed by
+ * a pair of hipEvents that its kernels record themselves (hipExtLaunchKernel):
+ * at the start of the stage's first kernel and the end of its last, so the
+ * time excludes the dispatch gap before the stage. moe_profile_read waits for
+ * the recorded events, writes the summed duration in milliseconds and the
+ * number of timed stage calls of each stage (arrays of `n` entries,
+ * n <= MOE_STAGE_COUNT), and resets the sums. It is off by default; while off,
+ * kernels launch plainly (and can be captured in graphs). State is
+ * process-wide; it is not meant for concurrent callers.
  */
 enum moe_stage {
     MOE_STAGE_ROUTER = 0,      /* K2 router logits */

@@ -519,7 +519,8 @@ STAGE_COUNT = 9
 
 
 def profile_enable(on: bool = True) -> None:
-    """Record a HIP event around every kernel launch of later calls."""
+    """Time each stage of later calls with events that its kernels record at
+    their own start and end."""
     _check(lib().moe_profile_enable(1 if on else 0))
 
 
