@@ -103,8 +103,16 @@ Layout layout(const moe_dims& d) {
 }
 
 // The one-block routing kernel covers small batches (decode).
+// The one-block routing kernel handles up to kSmallRoutePairs pairs, but its
+// time grows with them (one block). Against the multi-block top-k + dispatch
+// kernels (about 13 us), measured with 16 experts: 6.4 and 9.7 us at 16 and 32
+// pairs, 14.7 us at 64 (with 4 experts it still wins there), 22 us at 128 and
+// 53 us at 512. It is chosen up to kSmallRouteMaxPairs.
+constexpr int64_t kSmallRouteMaxPairs = 64;
+static_assert(kSmallRouteMaxPairs <= moe::kSmallRoutePairs, "within the kernel's capacity");
+
 bool small_routing(const moe_dims& d) {
-    return d.T * d.E <= moe::kSmallRouteLogits && d.T * d.top_k <= moe::kSmallRoutePairs;
+    return d.T * d.E <= moe::kSmallRouteLogits && d.T * d.top_k <= kSmallRouteMaxPairs;
 }
 
 // MOE_PATH_AUTO: the streaming decode path for small batches; the hybrid path

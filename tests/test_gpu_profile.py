@@ -12,25 +12,27 @@ from gpu_util import build_layer, say
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
-# pairs per expert from a few hundred down to one and zero; T*E and T*k small
-# enough for the one-block routing kernel, which also dispatches
+# pairs per expert from a few hundred down to one and zero (600 pairs: the
+# top-k and dispatch kernels)
 MIXED = W.config(0).with_(T=300, E=12, top_k=2, bias="zipf", bias_param=0.6)
-# T*E past the one-block routing: separate top-k and dispatch kernels
+# 32 pairs: the one-block routing kernel, which also dispatches
+SMALL = W.config(0).with_(T=16, E=12, top_k=2)
 LARGE = W.config(0).with_(T=1100, E=8, top_k=1)
+ROUTE = {"router", "topk", "dispatch"}
 CASES = {
-    "decode": (MIXED, {"router", "topk", "decode_up", "decode_down", "combine"}),
-    "prefill": (MIXED, {"router", "topk", "grouped_up", "grouped_down", "combine"}),
-    "hybrid": (MIXED, {"router", "topk", "grouped_up", "grouped_down", "decode_up",
-                       "decode_down", "combine"}),
-    "prefill_wide": (LARGE, {"router", "topk", "dispatch", "grouped_up", "grouped_down",
-                             "combine"}),
+    "decode, one-block routing": (SMALL, "decode",
+                                  {"router", "topk", "decode_up", "decode_down", "combine"}),
+    "decode": (MIXED, "decode", ROUTE | {"decode_up", "decode_down", "combine"}),
+    "prefill": (MIXED, "prefill", ROUTE | {"grouped_up", "grouped_down", "combine"}),
+    "hybrid": (MIXED, "hybrid", ROUTE | {"grouped_up", "grouped_down", "decode_up",
+                                         "decode_down", "combine"}),
+    "prefill_wide": (LARGE, "prefill_wide", ROUTE | {"grouped_up", "grouped_down", "combine"}),
 }
 
 
-@pytest.mark.parametrize("path", sorted(CASES))
-def test_profile_times_each_stage(path):
-    cfg, expected = CASES[path]
-    assert cfg.T * cfg.E > 8192 or "dispatch" not in expected
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_profile_times_each_stage(case):
+    cfg, path, expected = CASES[case]
     layer = build_layer(cfg)
     ws = moe.alloc_workspace(cfg.T, cfg.d, cfg.E, cfg.h, cfg.top_k, layer.dev)
 
