@@ -56,6 +56,9 @@ SMALL = {
     # pairs per expert 283/189/66/31/15/8/3/1/1/2/1/0: GEMM tiles, two-chunk and
     # one-chunk streamed experts and an empty one on the hybrid path
     "mixed expert sizes": W.config(0).with_(T=300, E=12, top_k=2, bias="zipf", bias_param=0.6),
+    # the largest expert count the library takes (kMaxExperts), top-8: 2400 pairs
+    # over 256 experts, most of them with a handful of rows
+    "256 experts, top-8": W.config(0).with_(T=300, d=256, E=256, h=256, top_k=8),
 }
 
 
