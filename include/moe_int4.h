@@ -298,6 +298,23 @@ enum moe_stage {
     MOE_STAGE_COUNT = 9
 };
 
+/*
+ * HBM measurement helpers for benchmarks (not part of the layer's arithmetic):
+ * the rates plain streaming reaches on the device, the practical ceiling beside
+ * the nominal peak. Device pointers, asynchronous on `stream`; bytes must be a
+ * positive multiple of 16 and the pointers 16-byte aligned (MOE_ERR_INVALID_ARG
+ * otherwise).
+ *   moe_hbm_read: reads every 16-byte word of buf once with the non-temporal
+ *     loads of the streaming decode kernels; block b of the launch writes the
+ *     XOR of the 32-bit words it read to sink[b] (sink: moe_hbm_read_sink_words()
+ *     uint32 words, caller-owned), so the XOR of all sink words is the XOR of
+ *     the buffer's words.
+ *   moe_hbm_copy: copies bytes from src to dst (buffers must not overlap).
+ */
+int moe_hbm_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+int moe_hbm_read_sink_words(void);
+int moe_hbm_copy(void *dst, const void *src, int64_t bytes, void *stream);
+
 int moe_profile_enable(int on);
 int moe_profile_read(double *ms, int64_t *launches, int n);
 const char *moe_stage_name(int stage);

@@ -83,6 +83,11 @@ def lib() -> ctypes.CDLL:
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_abi_version.restype = ctypes.c_int
         L.moe_device_check.restype = ctypes.c_int
+        L.moe_hbm_read.argtypes = [P, i64, P, P]
+        L.moe_hbm_read.restype = ctypes.c_int
+        L.moe_hbm_read_sink_words.restype = ctypes.c_int
+        L.moe_hbm_copy.argtypes = [P, P, i64, P]
+        L.moe_hbm_copy.restype = ctypes.c_int
         L.moe_quantize_int4.argtypes = [P, i64, i64, i32, P, P, P]
         L.moe_quantize_int4.restype = ctypes.c_int
         L.moe_quantize_int4_tiled.argtypes = [P, i64, i64, i32, P, P, P]
@@ -516,6 +521,28 @@ def unpack_int4(q: torch.Tensor) -> torch.Tensor:
 # ------------------------------------------------------------------ timing
 
 STAGE_COUNT = 9
+
+
+def hbm_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Stream every 16-byte word of `buf` once (measurement helper); each block
+    writes the XOR of the words it read into `sink` (uint32/int32,
+    ``hbm_read_sink_words()`` entries)."""
+    if not buf.is_cuda or not sink.is_cuda or sink.numel() < hbm_read_sink_words():
+        raise ValueError("buf and sink must be device tensors, sink of hbm_read_sink_words() words")
+    _check(lib().moe_hbm_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                              _stream(buf.device)))
+
+
+def hbm_read_sink_words() -> int:
+    return int(lib().moe_hbm_read_sink_words())
+
+
+def hbm_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    """Copy `src` into `dst` with the library's plain copy kernel (measurement helper)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not dst.is_cuda or not src.is_cuda:
+        raise ValueError("dst and src must be device tensors of the same size")
+    _check(lib().moe_hbm_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(src.device)))
 
 
 def profile_enable(on: bool = True) -> None:

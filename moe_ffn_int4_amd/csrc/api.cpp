@@ -835,6 +835,33 @@ int moe_forward(const moe_dims* dims, const uint16_t* x, const float* router_w,
                             MOE_PATH_AUTO, workspace, workspace_bytes, stream);
 }
 
+static int stream_args(const void* a, const void* b, int64_t bytes) {
+    if (!a || !b) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+    if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) % 16)
+        return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    if (bytes <= 0 || bytes % 16)
+        return fail(MOE_ERR_INVALID_ARG, "bytes = %lld must be a positive multiple of 16", (long long)bytes);
+    return MOE_OK;
+}
+
+int moe_hbm_read_sink_words(void) { return moe::kStreamBlocks; }
+
+int moe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+    g_last_error.clear();
+    CHECK(device_ok());
+    CHECK(stream_args(buf, sink, bytes));
+    HIP_CHECK(moe::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)), "read launch");
+    return MOE_OK;
+}
+
+int moe_hbm_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+    g_last_error.clear();
+    CHECK(device_ok());
+    CHECK(stream_args(dst, src, bytes));
+    HIP_CHECK(moe::launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream)), "copy launch");
+    return MOE_OK;
+}
+
 int moe_profile_enable(int on) {
     Prof& P = prof();
     std::lock_guard<std::mutex> lock(P.mu);

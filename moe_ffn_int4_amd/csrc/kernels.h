@@ -183,6 +183,14 @@ hipError_t launch_decode_up(const DecodeArgs& a, int max_chunks, int shared_chun
 hipError_t launch_decode_down(const DecodeArgs& a, int max_chunks, int shared_chunks,
                               hipStream_t stream);
 
+// Measurement kernels (stream.hip): read every 16-byte word of buf (bytes % 16
+// == 0) and write one XOR per block to sink[block] (kStreamBlocks words at most),
+// or copy bytes from src to dst
+constexpr int kStreamBlocks = 4096;
+unsigned stream_blocks(int64_t n16);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
 // K6c: y[t] = O[P + t] + sum_j gate[t, j] * O[inv[t, j]]  -> bf16
 hipError_t launch_combine(const float* O, const float* gates, const int32_t* inv, int64_t T,
                           int64_t P, int top_k, int64_t d, uint16_t* y, hipStream_t stream);
