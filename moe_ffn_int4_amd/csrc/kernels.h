@@ -186,7 +186,7 @@ hipError_t launch_decode_down(const DecodeArgs& a, int max_chunks, int shared_ch
 // Measurement kernels (stream.hip): read every 16-byte word of buf (bytes % 16
 // == 0) and write one XOR per block to sink[block] (kStreamBlocks words at most),
 // or copy bytes from src to dst
-constexpr int kStreamBlocks = 4096;
+constexpr int kStreamBlocks = 32768;  // best of 1024-32768 in a sweep of the read
 unsigned stream_blocks(int64_t n16);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
