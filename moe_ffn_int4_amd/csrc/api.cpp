@@ -50,10 +50,13 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// largest P + T whose down projection splits its reduction (workspace for O2)
+constexpr int64_t kSplitRows = 2048;
+
 // Workspace sections (byte offsets from the workspace base).
 struct Layout {
     size_t partials, logits, ids, gates, counts, offsets, tile_base, perm, inv, chunks, nchunks,
-        wparts, routing_end, x_perm, H, O, total;
+        wparts, routing_end, x_perm, H, O, O2, total;
     size_t xq, sxq, hq, shq, total_fp8;  // fp8 experts: quantized x and H rows, row scales
     int slices;
     int max_chunks;
@@ -93,6 +96,8 @@ Layout layout(const moe_dims& d) {
     L.x_perm = take(T * static_cast<size_t>(d.d) * 2);
     L.H = take((P + T) * static_cast<size_t>(d.h) * 2);
     L.O = take((P + T) * static_cast<size_t>(d.d) * 4);
+    // the streaming down projection's second partial sums (small batches only)
+    L.O2 = take(static_cast<int64_t>(P + T) <= kSplitRows ? (P + T) * static_cast<size_t>(d.d) * 4 : 0);
     L.total = off;
     L.xq = take(T * static_cast<size_t>(d.d));
     L.sxq = take(T * 4);
@@ -560,6 +565,12 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
 
     const bool decode =
         path == MOE_PATH_DECODE || (path == MOE_PATH_AUTO && P <= kDecodeMaxPairs);
+    // decode path, int4 groups of 128 without sliced staging (P < 4 E): the down
+    // projection splits its reduction over two blocks per chunk (twice the blocks
+    // of a launch that otherwise leaves HBM underused), the second half into O2
+    float* O2 = (decode && ex4 && d.group_size == moe::kGroup && P < 4 * d.E &&
+                 P + d.T <= kSplitRows && d.h >= 2 * moe::kGroup)
+                    ? reinterpret_cast<float*>(base + L.O2) : nullptr;
     const bool hybrid = !decode && (path == MOE_PATH_HYBRID ||
                                     (path == MOE_PATH_AUTO && P < kHybridAvgPairs * d.E));
     const int small_rows = decode ? -1 : (hybrid ? kHybridRows : 0);
@@ -659,6 +670,7 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         }
         a.sh0 = sh->s2;
         a.o_out = O;
+        a.o_out2 = st == s ? O2 : nullptr;  // never on the hybrid path's side stream
         return timed(MOE_STAGE_DECODE_DOWN, st, "decode down launch",
                      [&] { return moe::launch_decode_down(a, max_chunks, shared_chunks, st); });
     };
@@ -776,7 +788,7 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
     }
 
     CHECK(timed(MOE_STAGE_COMBINE, s, "combine launch", [&] {
-        return moe::launch_combine(O, R.gates, R.inv, d.T, P, d.top_k, d.d, y, s);
+        return moe::launch_combine(O, decode ? O2 : nullptr, R.gates, R.inv, d.T, P, d.top_k, d.d, y, s);
     }));
     return MOE_OK;
 }

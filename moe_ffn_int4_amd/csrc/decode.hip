@@ -379,6 +379,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const int l16 = lane & 15, kq = lane >> 4;
     const int64_t n = static_cast<int64_t>(blockIdx.x) * 64 + (narrow ? wave : sub) * 16 + l16;  // B column
     const int ng = static_cast<int>(K / kGroup);
+    // Reduction split over the grid's z dimension (the host launches two for
+    // the down projection of small batches, int4 groups of 128): this block
+    // sums groups glo .. ghi - 1 and stores its partial sums to o_out (z = 0)
+    // or o_out2 (z = 1), which the combine adds.
+    const int kz = static_cast<int>(blockIdx.z), nkz = static_cast<int>(gridDim.z);
+    const int glo = (kz * ng) / nkz, ghi = ((kz + 1) * ng) / nkz, ngl = ghi - glo;  // ngl may be 0
 
     // A row of MFMA row l16: int4 routed experts read the interleaved copy, bf16
     // weights the natural one. Rows past the chunk repeat its last row: their
@@ -445,9 +451,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         const uint8_t* q1 = UP ? a.wq1 + rb * ng * 1024 + kq * 256 + l16 * 16 : nullptr;
         const float* s0 = a.ws0 + (rb * ng * 16 + l16) * S;
         const float* s1 = UP ? a.ws1 + (rb * ng * 16 + l16) * S : nullptr;
+        q0 += static_cast<int64_t>(glo) * 1024;  // this block's groups (z split)
+        if (UP) q1 += static_cast<int64_t>(glo) * 1024;
+        s0 += static_cast<int64_t>(glo) * 16 * S;
+        if (UP) s1 += static_cast<int64_t>(glo) * 16 * S;
         WeightSlot<S> sl[U];
 #pragma unroll
-        for (int p = 0; p < D; ++p) load_weights<UP, S>(sl[p], q0, q1, s0, s1, min(p, ng - 1));
+        for (int p = 0; p < D; ++p) load_weights<UP, S>(sl[p], q0, q1, s0, s1, min(p, ngl > 0 ? ngl - 1 : 0));
         const int64_t pitch = K + 8;  // 16-byte pad between rows
         for (int64_t idx = tid; idx < static_cast<int64_t>(nrows) * (K / 8); idx += NT) {
             const int r = static_cast<int>(idx / (K / 8));
@@ -457,18 +467,18 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
                 *reinterpret_cast<const uint4*>(a.a_perm + srow * K + col);
         }
         __syncthreads();
-        const uint16_t* lrow = a_lds + m * pitch + (S == 1 ? kq * 32 : kq * 8);
-        const int full = ng - ng % U;
+        const uint16_t* lrow = a_lds + m * pitch + (S == 1 ? kq * 32 : kq * 8) + glo * kGroup;
+        const int full = ngl - ngl % U;
         for (int g0 = 0; g0 < full; g0 += U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                load_weights<UP, S>(sl[(u + D) % U], q0, q1, s0, s1, min(g0 + u + D, ng - 1));
+                load_weights<UP, S>(sl[(u + D) % U], q0, q1, s0, s1, min(g0 + u + D, ngl - 1));
                 compute_lds<UP, S>(sl[u], lrow, g0 + u, acc0, acc1);
             }
         }
 #pragma unroll
         for (int u = 0; u < D; ++u)
-            if (u < ng - full) compute_lds<UP, S>(sl[u], lrow, full + u, acc0, acc1);
+            if (u < ngl - full) compute_lds<UP, S>(sl[u], lrow, full + u, acc0, acc1);
     } else if (int4 && SL) {
         // Chunks of more than lds_rows rows: the block stages A in slices of SG
         // groups (SG * 128 columns of the chunk's rows). Two slices sit in LDS:
@@ -566,26 +576,31 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         // it (cache hits), so every loop iteration issues the same loads and the
         // compiler can wait on exact load counts; full rounds of U groups run
         // without guards, the last ng % U groups are already in their slots.
+        q0 += static_cast<int64_t>(glo) * 1024;  // this block's groups (z split)
+        if (UP) q1 += static_cast<int64_t>(glo) * 1024;
+        s0 += static_cast<int64_t>(glo) * 16 * S;
+        if (UP) s1 += static_cast<int64_t>(glo) * 16 * S;
+        const uint16_t* arow_k = arow + glo * kGroup;
         RoutedSlot<S> sl[U];
 #pragma unroll
-        for (int p = 0; p < D; ++p) load_routed<UP, S>(sl[p], q0, q1, s0, s1, arow, min(p, ng - 1));
-        const int full = ng - ng % U;
+        for (int p = 0; p < D; ++p) load_routed<UP, S>(sl[p], q0, q1, s0, s1, arow_k, min(p, ngl > 0 ? ngl - 1 : 0));
+        const int full = ngl - ngl % U;
         for (int g0 = 0; g0 < full; g0 += U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                load_routed<UP, S>(sl[(u + D) % U], q0, q1, s0, s1, arow, min(g0 + u + D, ng - 1));
+                load_routed<UP, S>(sl[(u + D) % U], q0, q1, s0, s1, arow_k, min(g0 + u + D, ngl - 1));
                 compute_routed<UP, S>(sl[u], acc0, acc1);
             }
         }
 #pragma unroll
         for (int u = 0; u < D; ++u)
-            if (u < ng - full) compute_routed<UP, S>(sl[u], acc0, acc1);
+            if (u < ngl - full) compute_routed<UP, S>(sl[u], acc0, acc1);
     } else {
         // this wave's quarter of the groups: gb .. gb + cnt - 1 (cnt may be 0)
         constexpr int D = DS;
         constexpr int U = D + 1;
-        const int gb = (wave * ng) / 4;
-        const int cnt = ((wave + 1) * ng) / 4 - gb;
+        const int gb = glo + (wave * ngl) / 4;
+        const int cnt = glo + ((wave + 1) * ngl) / 4 - gb;
         const int last = cnt > 0 ? cnt - 1 : 0;
         const int64_t rb = n >> 4;
         const int64_t mat = routed ? static_cast<int64_t>(group) * N * K : 0;  // expert's matrix
@@ -640,7 +655,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         if (mr >= nrows) continue;
         const int64_t orow = row0 + mr;
         if (UP) a.h_out[orow * N + hcol] = f32_to_bf16(siluf_(acc0[r]) * acc1[r]);
-        else a.o_out[orow * N + n] = acc0[r];
+        else (kz ? a.o_out2 : a.o_out)[orow * N + n] = acc0[r];
     }
 }
 
@@ -669,7 +684,10 @@ static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, int shar
     static_assert(!SL || (S == 1 && !F8), "sliced staging: int4 groups of 128");
     constexpr size_t sliced = SL ? slice_lds_bytes(slice_groups(UP, DL)) : 0;
     if (a.lds_rows < kDecodeRows && lds < sliced) lds = sliced;
-    dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks + 3 * shared_chunks));
+    // two blocks per chunk and feature range, each half the reduction, when the
+    // host gives a second output (down projection, int4 groups of 128)
+    const unsigned zs = (!UP && !F8 && !SL && S == 1 && a.o_out2) ? 2u : 1u;
+    dim3 grid(static_cast<unsigned>(a.N / 64), static_cast<unsigned>(max_chunks + 3 * shared_chunks), zs);
     MOE_LAUNCH((decode_kernel<UP, DR, DS, DL, F8, S, SL>), grid, dim3(NT), lds, stream, a);
     return hipGetLastError();
 }

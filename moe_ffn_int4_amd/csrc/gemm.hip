@@ -482,6 +482,7 @@ hipError_t launch_grouped_down(const GroupedGemmArgs& a, hipStream_t stream) {
 // y[t] = O[P + t] + sum_j gate[t, j] * O[inv[t * k + j]], j ascending, fp32, then
 // bf16 (round to nearest even). One thread per 4 consecutive columns.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ O,
+                                                      const float* __restrict__ O2,
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ inv, int64_t T,
                                                       int64_t P, int top_k, int64_t d,
@@ -491,11 +492,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (q >= T * per_row) return;
     const int64_t t = q / per_row;
     const int64_t c = (q - t * per_row) * 4;
-    float4 acc = *reinterpret_cast<const float4*>(O + (P + t) * d + c);
+    // a row of O, plus its second partial sums when the down projection split
+    // its reduction (added first, in this fixed order)
+    auto row = [&](int64_t r) {
+        float4 v = *reinterpret_cast<const float4*>(O + r * d + c);
+        if (O2) {
+            const float4 w = *reinterpret_cast<const float4*>(O2 + r * d + c);
+            v.x += w.x;
+            v.y += w.y;
+            v.z += w.z;
+            v.w += w.w;
+        }
+        return v;
+    };
+    float4 acc = row(P + t);
     for (int j = 0; j < top_k; ++j) {
         const float g = gates[t * top_k + j];
         const int64_t slot = inv[t * top_k + j];
-        const float4 o = *reinterpret_cast<const float4*>(O + slot * d + c);
+        const float4 o = row(slot);
         acc.x = fmaf(g, o.x, acc.x);
         acc.y = fmaf(g, o.y, acc.y);
         acc.z = fmaf(g, o.z, acc.z);
@@ -507,11 +521,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     *reinterpret_cast<uint2*>(y + t * d + c) = out;
 }
 
-hipError_t launch_combine(const float* O, const float* gates, const int32_t* inv, int64_t T,
-                          int64_t P, int top_k, int64_t d, uint16_t* y, hipStream_t stream) {
+hipError_t launch_combine(const float* O, const float* O2, const float* gates, const int32_t* inv,
+                          int64_t T, int64_t P, int top_k, int64_t d, uint16_t* y, hipStream_t stream) {
     const int64_t n = T * (d / 4);
     MOE_LAUNCH(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                       stream, O, gates, inv, T, P, top_k, d, y);
+                       stream, O, O2, gates, inv, T, P, top_k, d, y);
     return hipGetLastError();
 }
 

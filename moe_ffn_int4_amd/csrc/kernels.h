@@ -172,6 +172,7 @@ struct DecodeArgs {
     const float* a8s;
     uint16_t* h_out;
     float* o_out;
+    float* o_out2;           // down: second half of the reduction's partial sums (null: no split)
     int sliced;              // int4 groups of 128: larger chunks stage A in LDS slices
     int lds_rows;            // set by the launcher: routed chunks this small stage A in LDS
     int max_chunks;          // set by the launcher: grid rows of the chunk list
@@ -192,7 +193,8 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hi
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 
 // K6c: y[t] = O[P + t] + sum_j gate[t, j] * O[inv[t, j]]  -> bf16
-hipError_t launch_combine(const float* O, const float* gates, const int32_t* inv, int64_t T,
-                          int64_t P, int top_k, int64_t d, uint16_t* y, hipStream_t stream);
+// (O2 non-null: the down projection's second partial sums, added to O first)
+hipError_t launch_combine(const float* O, const float* O2, const float* gates, const int32_t* inv,
+                          int64_t T, int64_t P, int top_k, int64_t d, uint16_t* y, hipStream_t stream);
 
 }  // namespace moe
