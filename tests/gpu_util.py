@@ -122,8 +122,12 @@ def oracle_forward_rows(layer: Layer, rows: np.ndarray, gpu_ids: Optional[np.nda
             ids = forced
     need = sorted(set(int(e) for e in np.unique(ids)))
     experts: List = [None] * cfg.E
-    for e in need:
+    for i, e in enumerate(need):
         experts[e] = oracle_expert(layer, e)
+        if len(need) > 16 and (i + 1) % 32 == 0:
+            say(f"  oracle: {i + 1}/{len(need)} experts quantized")
+    if len(rows) > 64:
+        say(f"  oracle: per-token loop over {len(rows)} tokens")
     r = native.moe_forward_per_token(xs, layer.wr.numpy(), b, cfg.top_k, experts, layer.shared,
                                      forced_ids=forced, group_size=layer.group)
     return r, margin
@@ -145,6 +149,109 @@ def check_ids(gpu_ids: np.ndarray, ref_ids: np.ndarray, margin: np.ndarray) -> i
     bad = np.nonzero(np.any(a != b, axis=1))[0]
     assert bad.size == 0, f"{bad.size} tokens with a clear margin chose different experts"
     return int((~sure).sum())
+
+
+# The library's AUTO path choice, as include/moe_int4.h documents it: the
+# streaming decode path up to 64 token-expert pairs; the hybrid path while the
+# pairs average under 256 per routed expert, whose routed experts with at most
+# 32 pairs are streamed in 16-row chunks beside the GEMMs; 256-row GEMM tiles
+# otherwise. GEMM row tiles are 128 rows (hybrid, prefill) or 256 (prefill_wide,
+# whose partial tiles of at most 128 rows run a half-tile body), so a row from
+# every 128-row piece of an expert's slots reaches every tile and both halves.
+DECODE_MAX_PAIRS, HYBRID_AVG_PAIRS, HYBRID_ROWS = 64, 256, 32
+ROW_PIECE, CHUNK_ROWS = 128, 16
+
+
+def resolved_path(T: int, E: int, top_k: int, path: str = "auto") -> str:
+    if path != "auto":
+        return path
+    P = T * top_k
+    if P <= DECODE_MAX_PAIRS:
+        return "decode"
+    return "hybrid" if P < HYBRID_AVG_PAIRS * E else "prefill_wide"
+
+
+@dataclass
+class Coverage:
+    rows: np.ndarray   # tokens to check, ascending
+    units: int         # work units (row pieces of GEMM tiles, streamed chunks)
+    report: str
+
+
+def covering_rows(ids: np.ndarray, E: int, path: str,
+                  extra: Optional[np.ndarray] = None) -> Coverage:
+    """Tokens whose rows reach every unit of work the GPU ran for this routing.
+
+    From the GPU's expert ids [T, k], the slots of each expert are its pairs
+    p = t * k + j in ascending order (the dispatch order). Units: every
+    ROW_PIECE-slot piece of each expert run on GEMM tiles (its ragged tail
+    included) and every CHUNK_ROWS-slot chunk of each streamed expert; the
+    shared expert's ROW_PIECE-token pieces (CHUNK_ROWS on the decode path).
+    Greedy: for each unit not yet reached, take the token of that unit that
+    reaches the most units not yet reached (the unit's last row on ties).
+    Every touched expert and every tile (so every XCD's range) then has a
+    checked row; the result is asserted here, independently of the greedy.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    P = T * k
+    pair_e = ids.reshape(-1)
+    if pair_e.min() < 0 or pair_e.max() >= E:
+        raise ValueError("expert id out of range")
+    order = np.argsort(pair_e, kind="stable")          # slot -> pair
+    counts = np.bincount(pair_e, minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    slot_of = np.empty(P, dtype=np.int64)
+    slot_of[order] = np.arange(P)
+    rank = slot_of - offsets[pair_e]                    # position inside its expert
+    if path == "decode":
+        usize = np.full(E, CHUNK_ROWS)
+        shared_size = CHUNK_ROWS
+    elif path == "hybrid":
+        usize = np.where(counts <= HYBRID_ROWS, CHUNK_ROWS, ROW_PIECE)
+        shared_size = ROW_PIECE
+    else:
+        usize = np.full(E, ROW_PIECE)
+        shared_size = ROW_PIECE
+    nunits = (counts + usize - 1) // usize
+    ubase = np.concatenate([[0], np.cumsum(nunits)])
+    n_routed = int(ubase[E])
+    n_shared = (T + shared_size - 1) // shared_size
+    pair_unit = ubase[pair_e] + rank // usize[pair_e]
+    token_units = np.concatenate(
+        [pair_unit.reshape(T, k), (n_routed + np.arange(T) // shared_size)[:, None]], axis=1)
+    covered = np.zeros(n_routed + n_shared, dtype=bool)
+    chosen = [] if extra is None else [int(t) for t in extra]
+    for t in chosen:
+        covered[token_units[t]] = True
+    for u in range(n_routed + n_shared):
+        if covered[u]:
+            continue
+        if u < n_routed:
+            e = int(np.searchsorted(ubase, u, side="right") - 1)
+            i = u - int(ubase[e])
+            lo = int(offsets[e]) + i * int(usize[e])
+            hi = min(lo + int(usize[e]), int(offsets[e + 1]))
+            cands = order[lo:hi][::-1] // k
+        else:
+            i = u - n_routed
+            cands = np.arange(i * shared_size, min((i + 1) * shared_size, T))[::-1]
+        gain = (~covered[token_units[cands]]).sum(axis=1)
+        t = int(cands[int(np.argmax(gain))])
+        chosen.append(t)
+        covered[token_units[t]] = True
+    rows = np.unique(np.asarray(chosen, dtype=np.int64))
+    # independent check: the chosen tokens' pairs reach every unit
+    reach = np.zeros_like(covered)
+    reach[token_units[rows].ravel()] = True
+    assert reach.all(), "coverage selection missed a unit"
+    touched = int((counts > 0).sum())
+    seen = len(set(ids[rows].ravel().tolist()))
+    streamed = int(((usize == CHUNK_ROWS) & (counts > 0)).sum()) if path != "decode" else touched
+    report = (f"coverage[{path}]: experts {seen}/{touched} touched, routed units {n_routed}/{n_routed} "
+              f"({streamed} experts in {CHUNK_ROWS}-row chunks, the rest in {ROW_PIECE}-row pieces), "
+              f"shared units {n_shared}/{n_shared}, {len(rows)} of {T} tokens")
+    return Coverage(rows, n_routed + n_shared, report)
 
 
 def sample_rows(T: int, n: int, seed: int = 0) -> np.ndarray:

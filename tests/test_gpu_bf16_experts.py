@@ -8,7 +8,8 @@ import torch
 
 import moe_ffn_int4_amd as moe
 import workloads as W
-from gpu_util import TOL, build_layer, check_ids, oracle_forward_rows, row_errors, sample_rows, say
+from gpu_util import (TOL, build_layer, check_ids, covering_rows, oracle_forward_rows,
+                      resolved_path, row_errors, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -50,14 +51,17 @@ def test_small_layers_every_token(name, path):
     _check(layer, y, ids, np.arange(cfg.T))
 
 
-@pytest.mark.parametrize("i,nrows", [(1, 16), (2, 24)])
-def test_benchmark_layers_sampled(i, nrows):
+@pytest.mark.parametrize("i", [1, 2, 3, 4])
+def test_benchmark_layers_covered(i):
     cfg = W.config(i)
-    say(f"forward bf16 experts: config {i} ({cfg.name}), {nrows} rows")
+    say(f"forward bf16 experts: config {i} ({cfg.name})")
     layer = build_layer(cfg, routed="bf16")
     y, ids = _run(layer)
     assert torch.isfinite(y.float()).all()
-    _check(layer, y, ids, sample_rows(cfg.T, nrows, seed=i))
+    cov = covering_rows(ids, cfg.E, resolved_path(cfg.T, cfg.E, cfg.top_k),
+                        extra=sample_rows(cfg.T, 4, seed=i))
+    say("  " + cov.report)
+    _check(layer, y, ids, cov.rows)
 
 
 def test_rejects_mismatched_experts():

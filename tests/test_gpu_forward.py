@@ -3,9 +3,12 @@
 Bar (stated for the layer): every output row within 2e-2 relative error in the
 infinity norm of the oracle's fp64 row; expert ids equal wherever the oracle's
 top-k margin exceeds 1e-4, and where it does not, the oracle is evaluated on the
-GPU's choice. Small layers are checked on every token; the 5120 x 8192 layers on
-sampled tokens (the first and last always included), each computed one by one
-by the oracle's per-token loop.
+GPU's choice. Small layers are checked on every token. The 5120 x 8192 layers
+are checked on a chosen set of tokens, each computed one by one by the oracle's
+per-token loop: a row from every 128-row piece of every expert's GEMM tiles
+(ragged tails included), every 16-row streamed chunk, and every row piece of
+the shared expert, so every touched expert, every tile and every XCD's range of
+tiles has a checked row (``covering_rows``), plus a few random tokens.
 """
 import numpy as np
 import pytest
@@ -13,8 +16,8 @@ import torch
 
 import moe_ffn_int4_amd as moe
 import workloads as W
-from gpu_util import (TOL, build_layer, check_ids, oracle_forward_rows, row_errors,
-                      sample_rows, say)
+from gpu_util import (TOL, build_layer, check_ids, covering_rows, oracle_forward_rows,
+                      resolved_path, row_errors, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -107,14 +110,17 @@ def test_tiny_layer_all_paths_agree():
         assert err.max() <= 1e-2, other
 
 
-@pytest.mark.parametrize("i,nrows", [(1, 16), (2, 48), (3, 48), (4, 12)])
-def test_benchmark_layers_sampled(i, nrows):
+@pytest.mark.parametrize("i", [1, 2, 3, 4])
+def test_benchmark_layers_covered(i):
     cfg = W.config(i)
-    say(f"forward: config {i} ({cfg.name}) T={cfg.T} E={cfg.E} k={cfg.top_k}, {nrows} rows")
+    say(f"forward: config {i} ({cfg.name}) T={cfg.T} E={cfg.E} k={cfg.top_k}")
     layer = build_layer(cfg)
     y, ids, gates = _run(layer)
     assert torch.isfinite(y.float()).all()
-    _check(layer, y, ids, sample_rows(cfg.T, nrows, seed=i))
+    cov = covering_rows(ids, cfg.E, resolved_path(cfg.T, cfg.E, cfg.top_k),
+                        extra=sample_rows(cfg.T, 8, seed=i))
+    say("  " + cov.report)
+    _check(layer, y, ids, cov.rows)
 
 
 def test_deterministic_and_reusable_workspace():

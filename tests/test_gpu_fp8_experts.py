@@ -10,7 +10,8 @@ import torch
 
 import moe_ffn_int4_amd as moe
 import workloads as W
-from gpu_util import TOL, build_layer, check_ids, oracle_forward_rows, row_errors, sample_rows, say
+from gpu_util import (TOL, build_layer, check_ids, covering_rows, oracle_forward_rows,
+                      resolved_path, row_errors, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -81,14 +82,17 @@ def test_paths_agree_and_workspace_reuse():
         assert row_errors(y1, y2.float().numpy().astype(np.float64)).max() <= 1e-2, other
 
 
-@pytest.mark.parametrize("i,nrows", [(1, 16), (2, 24), (3, 16)])
-def test_benchmark_layers_sampled(i, nrows):
+@pytest.mark.parametrize("i", [1, 2, 3, 4])
+def test_benchmark_layers_covered(i):
     cfg = W.config(i)
-    say(f"forward fp8 experts: config {i} ({cfg.name}), {nrows} rows")
+    say(f"forward fp8 experts: config {i} ({cfg.name})")
     layer = build_layer(cfg, routed="fp8")
     y, ids = _run(layer)
     assert torch.isfinite(y.float()).all()
-    _check(layer, y, ids, sample_rows(cfg.T, nrows, seed=i))
+    cov = covering_rows(ids, cfg.E, resolved_path(cfg.T, cfg.E, cfg.top_k),
+                        extra=sample_rows(cfg.T, 4, seed=i))
+    say("  " + cov.report)
+    _check(layer, y, ids, cov.rows)
 
 
 def test_rejects_small_workspace_and_bad_bound():

@@ -14,7 +14,8 @@ import torch
 
 import moe_ffn_int4_amd as moe
 import workloads as W
-from gpu_util import TOL, build_layer, check_ids, oracle_forward_rows, row_errors, sample_rows, say
+from gpu_util import (TOL, build_layer, check_ids, covering_rows, oracle_forward_rows,
+                      resolved_path, row_errors, sample_rows, say)
 from oracle import int4_group_quantize
 
 pytestmark = pytest.mark.gpu
@@ -91,12 +92,15 @@ def test_small_layers_every_token(g, name, path):
     _check(layer, y, ids, np.arange(cfg.T))
 
 
-@pytest.mark.parametrize("g", GROUPS)
-@pytest.mark.parametrize("i,nrows", [(1, 16), (2, 24)])
-def test_benchmark_layers_sampled(g, i, nrows):
+# every benchmark layer at groups of 32, the Scout layers at groups of 64 too
+@pytest.mark.parametrize("g,i", [(64, 1), (64, 2), (32, 1), (32, 2), (32, 3), (32, 4)])
+def test_benchmark_layers_covered(g, i):
     cfg = W.config(i)
-    say(f"forward g={g}: config {i} ({cfg.name}), {nrows} rows")
+    say(f"forward g={g}: config {i} ({cfg.name})")
     layer = build_layer(cfg, group=g)
     y, ids = _run(layer)
     assert torch.isfinite(y.float()).all()
-    _check(layer, y, ids, sample_rows(cfg.T, nrows, seed=i))
+    cov = covering_rows(ids, cfg.E, resolved_path(cfg.T, cfg.E, cfg.top_k),
+                        extra=sample_rows(cfg.T, 4, seed=i))
+    say("  " + cov.report)
+    _check(layer, y, ids, cov.rows)
