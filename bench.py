@@ -59,12 +59,20 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--prefill", default=None,
+                    help="comma-separated prefill layers also timed in the same run and "
+                         "reported under `prefill` (default with the decode layer: 2,3,4; "
+                         "'' for none)")
+    ap.add_argument("--no-quantizer", action="store_true", help="skip the K1 quantizer leg")
     ap.add_argument("--stage-timing", default="separate", choices=["separate", "inline"],
                     help="per-kernel HIP events in a second pass (separate) or in the timed "
                          "loop itself (inline)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each layer copy's forward as a captured HIP graph")
-    return ap.parse_args()
+    a = ap.parse_args()
+    if a.prefill is None:
+        a.prefill = "2,3,4" if a.config == 1 else ""
+    return a
 
 
 STAGE_TRAFFIC_KEY = {"decode_up": "decode_up", "grouped_up": "grouped_up"}
@@ -277,41 +285,70 @@ def cpu_baseline(layer, n_sample, dev, min_seconds=10.0):
         if dt >= min_seconds or reps >= 1000:
             break
     cores = len(os.sched_getaffinity(0))
-    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
-        cores = min(cores, int(os.environ["OMP_NUM_THREADS"]))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit():
+        cores = min(cores, int(omp))
     return ref, rows, {
         "value": n * reps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "cpu_model": cpu_model(), "omp_num_threads": omp or None,
         "sample": f"{n} of the {cfg.T} tokens of the first layer copy (fp64 per-token C loop, "
                   f"{len(set(ids.ravel().tolist()))} experts), run {reps} times; {dt:.2f} s wall",
     }
 
 
-def main() -> int:
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one MI355X: this build runs on a single GPU; "
-              "--gpus must be 1 (multi-GPU expert parallelism is design-only here).",
-              file=sys.stderr)
-        return 2
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def quantizer_leg(dev, reps: int = 20):
+    """K1 alone: one 8192 x 5120 fp32 expert matrix (a W1 of the benchmark
+    layers) quantized to int4 g128, row-major and tiled. Algorithmic bytes per
+    call: 4 B read + 0.5 B codes + 4/128 B of scale written per weight."""
+    import torch
+    import moe_ffn_int4_amd as moe
+    rows, K = 8192, 5120
+    ws = [torch.randn(rows, K, device=dev) * 0.02 for _ in range(4)]  # 671 MB: past the LLC
+    q = torch.empty(rows, K // 2, dtype=torch.uint8, device=dev)
+    sc = torch.empty(rows, K // 128, dtype=torch.float32, device=dev)
+    nbytes = rows * K * (4 + 0.5 + 4 / 128)
+    out = {"matrix": f"{rows} x {K} fp32 -> int4 g128", "algorithmic_bytes": nbytes}
+    for tiled in (False, True):
+        for i in range(4):
+            moe.quantize_int4(ws[i], q, sc, tiled=tiled)
+        torch.cuda.synchronize()
+        # one kernel per call on torch's current stream: events around the calls
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(reps):
+            moe.quantize_int4(ws[i % 4], q, sc, tiled=tiled)
+        end.record()
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) * 1e3 / reps
+        out["tiled" if tiled else "row_major"] = {"us_per_call": us, "GBps": nbytes / us / 1e3,
+                                                  "frac_of_peak": nbytes / us / 1e3 / HBM_PEAK_GBPS}
+    del ws, q, sc
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure(ci: int, args, steps: int, warmup: int, cpu_sample: int, cpu_seconds: float,
+            with_ceiling: bool):
+    """Time `steps` forwards of benchmark layer `ci` (after `warmup`), per-stage
+    kernel times, the dominant kernel's roofline and (optionally) the oracle
+    baseline on a sample of the first layer copy; frees the layers after."""
     import numpy as np
     import torch
     import moe_ffn_int4_amd as moe
     import workloads as W
 
-    if not os.path.exists(moe.LIB_PATH):
-        from moe_ffn_int4_amd import build as _b
-        _b.build()
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if moe.lib().moe_device_check() != 0:
-        raise SystemExit(f"not a gfx950 device: {moe.lib().moe_last_error().decode()}")
-
-    ci = args.config
     cfg0 = W.config(ci)
-    steps = args.steps if args.steps is not None else DEFAULT_STEPS[ci]
-    warmup = args.warmup if args.warmup is not None else DEFAULT_WARMUP[ci]
     nlayers = args.layers or max(2, min(8, math.ceil(
         4e9 / layer_weight_bytes(cfg0, args.experts, args.group))))
     print(f"[bench] config {ci} {cfg0.name}: T={cfg0.T} d={cfg0.d} E={cfg0.E} h={cfg0.h} "
@@ -375,8 +412,8 @@ def main() -> int:
         stages = moe.profile_read()
         moe.profile_enable(False)
     else:
-        # the same steps again, eagerly, with a HIP event recorded around every
-        # kernel launch on the forward's stream: per-kernel durations
+        # the same steps again, eagerly, with the kernels recording HIP events
+        # at their own start and end: per-kernel durations
         moe.profile_enable(True)
         moe.profile_read()
         for i in range(steps):
@@ -386,55 +423,127 @@ def main() -> int:
         moe.profile_enable(False)
     wall = t1 - t0
     ms_per_step = wall * 1e3 / steps
-    value = cfg0.T * steps / wall
 
-    # roofline of the dominant kernel, per launch, averaged over the timed steps
     units = [stage_units(L["cfg"], c, args.experts, args.group, args.path) for L, c in zip(layers, counts)]
     launched = {k: v for k, v in stages.items() if v[1] > 0}
-    dom = max(launched, key=lambda k: launched[k][0])
-    dom_ms, dom_n = launched[dom]
-    per_step = [u.get(dom, (0, 0.0)) for u in units]
-    # launches of step i use layer copy i % nlayers
-    byts = sum(per_step[i % nlayers][0] for i in range(steps)) / steps
-    flops = sum(per_step[i % nlayers][1] for i in range(steps)) / steps
-    mean_s = dom_ms / dom_n / 1e3
     decode_like = cfg0.T * cfg0.top_k < 1024
-    if decode_like:
-        achieved = byts / mean_s / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
-    else:
-        achieved = flops / mean_s / 1e12
-        # the launch's FLOPs at their own dtype's peak: fp8 routed rows, bf16 the rest
-        f8 = sum(units[i % nlayers]["fp8_flops"].get(dom, 0.0) for i in range(steps)) / steps
-        peak = flops / ((flops - f8) / BF16_MFMA_PEAK_TFLOPS + f8 / FP8_MFMA_PEAK_TFLOPS)
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak,
-                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None}
-    roof["traffic"] = measured_traffic(
-        dom, cfg0.name if (args.experts == "int4" and args.group == 128) else None)
-    if roof["traffic"] is not None:
-        roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
-    roof["kernel"] = dom
-    roof["mean_launch_us"] = mean_s * 1e6
-    roof["algorithmic_per_launch"] = byts if decode_like else flops
-    ceiling = hbm_ceiling(dev)
-    if decode_like:
+
+    def roofline(stage):
+        """algorithmic bytes (decode) or FLOPs (prefill) of one launch of
+        `stage`, averaged over the timed steps, over its mean launch time"""
+        st_ms, st_n = launched[stage]
+        per_step = [u.get(stage, (0, 0.0)) for u in units]
+        byts = sum(per_step[i % nlayers][0] for i in range(steps)) / steps
+        flops = sum(per_step[i % nlayers][1] for i in range(steps)) / steps
+        mean_s = st_ms / st_n / 1e3
+        if decode_like:
+            achieved = byts / mean_s / 1e9
+            roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
+        else:
+            achieved = flops / mean_s / 1e12
+            # the launch's FLOPs at their own dtype's peak: fp8 routed rows, bf16 the rest
+            f8 = sum(units[i % nlayers]["fp8_flops"].get(stage, 0.0) for i in range(steps)) / steps
+            peak = flops / ((flops - f8) / BF16_MFMA_PEAK_TFLOPS + f8 / FP8_MFMA_PEAK_TFLOPS)
+            roof = {"bound": "mfma", "achieved": achieved, "peak": peak,
+                    "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None}
+        roof["traffic"] = measured_traffic(
+            stage, cfg0.name if (args.experts == "int4" and args.group == 128) else None)
+        if roof["traffic"] is not None:
+            roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
+        roof["kernel"] = stage
+        roof["mean_launch_us"] = mean_s * 1e6
+        roof["algorithmic_per_launch"] = byts if decode_like else flops
+        return roof
+
+    # the dominant kernel: the longest stage; on prefill layers the up projection's GEMM
+    dom = max(launched, key=lambda k: launched[k][0])
+    if not decode_like and "grouped_up" in launched:
+        dom = "grouped_up"
+    roof = roofline(dom)
+    ceiling = hbm_ceiling(dev) if with_ceiling else None
+    if decode_like and ceiling:
         # how much of plain streaming the kernel reaches (the nominal peak stays `peak`)
-        roof["practical_hbm"] = dict(ceiling, frac_of_read=achieved / ceiling["read_GBps"])
+        roof["practical_hbm"] = dict(ceiling, frac_of_read=roof["achieved"] / ceiling["read_GBps"])
 
     step_bytes = sum(units[i % nlayers]["step_bytes"] for i in range(steps)) / steps
     detail = {
         "stages_us_per_step": {k: round(v[0] * 1e3 / steps, 2) for k, v in launched.items()},
+        # the whole layer: algorithmic bytes of every stage's weights and
+        # activations over the wall-clock step
         "step_hbm_GBps": step_bytes / (wall / steps) / 1e9,
+        "step_hbm_frac": step_bytes / (wall / steps) / 1e9 / HBM_PEAK_GBPS,
         "step_TFLOPs": cfg0.flops() / (wall / steps) / 1e12,
         "touched_experts": [u["touched"] for u in units],
         "layer_copies": nlayers,
         "path": args.path,
         "graph": bool(args.graph),
         "stage_timing": args.stage_timing,
-        "practical_hbm": ceiling,
     }
+    if ceiling:
+        detail["practical_hbm"] = ceiling
+    if "grouped_down" in launched and not decode_like:
+        detail["grouped_down_roofline"] = {k: v for k, v in roofline("grouped_down").items()
+                                           if k in ("achieved", "peak", "frac", "mean_launch_us")}
 
+    base = None
+    if cpu_sample > 0:
+        ref, rows, base = cpu_baseline(layers[0], cpu_sample, dev, min_seconds=cpu_seconds)
+        # spot parity of the same tokens on the GPU (layer copy 0)
+        step(0)
+        torch.cuda.synchronize()
+        yg = y[torch.as_tensor(rows, device=dev)].float().cpu().numpy().astype(np.float64)
+        err = np.abs(yg - ref.y).max(axis=1) / np.maximum(np.abs(ref.y).max(axis=1), 1e-6)
+        base["gpu_vs_oracle_max_row_rel_err"] = float(err.max())
+
+    res = {"cfg": cfg0, "steps": steps, "warmup": warmup, "ms_per_step": ms_per_step,
+           "value": cfg0.T * steps / wall, "roofline": roof, "detail": detail, "cpu_baseline": base}
+    del layers, ws, y, ids, graphs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def workload_name(cfg0, args) -> str:
+    import workloads as W
+    return (f"{cfg0.name}: T={cfg0.T} d={cfg0.d} E={cfg0.E}+1 shared h={cfg0.h} top_k={cfg0.top_k}, "
+            + {"int4": f"int4 g{args.group}", "bf16": "bf16",
+               "fp8": f"fp8 row-wise (act ub {W.FP8_ACT_UB:g})"}[args.experts]
+            + " routed / bf16 shared")
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one MI355X: this build runs on a single GPU; "
+              "--gpus must be 1 (multi-GPU expert parallelism is design-only here).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import moe_ffn_int4_amd as moe
+
+    if not os.path.exists(moe.LIB_PATH):
+        from moe_ffn_int4_amd import build as _b
+        _b.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if moe.lib().moe_device_check() != 0:
+        raise SystemExit(f"not a gfx950 device: {moe.lib().moe_last_error().decode()}")
+
+    ci = args.config
+    steps = args.steps if args.steps is not None else DEFAULT_STEPS[ci]
+    warmup = args.warmup if args.warmup is not None else DEFAULT_WARMUP[ci]
+    n_sample = 0 if args.no_cpu_baseline else (args.cpu_sample or None)
+    import workloads as W
+    cfg0 = W.config(ci)
+    decode_like = cfg0.T * cfg0.top_k < 1024
+    if n_sample is None:
+        n_sample = 16 if decode_like else 8
+    head = measure(ci, args, steps, warmup, n_sample, 10.0, with_ceiling=True)
+
+    detail = head["detail"]
     if args.copy_calibration:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -444,31 +553,52 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         detail["copy_calibration_bytes"] = n
+        del src, dst
 
     out = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8+bf16" if args.experts == "fp8" else "bf16", "data": "synthetic",
-        "config": {"workload": f"{cfg0.name}: T={cfg0.T} d={cfg0.d} E={cfg0.E}+1 shared "
-                               f"h={cfg0.h} top_k={cfg0.top_k}, "
-                               + {"int4": f"int4 g{args.group}", "bf16": "bf16",
-                                  "fp8": f"fp8 row-wise (act ub {W.FP8_ACT_UB:g})"}[args.experts]
-                               + " routed / bf16 shared",
+        "config": {"workload": workload_name(cfg0, args),
                    "T": cfg0.T, "d": cfg0.d, "E": cfg0.E, "h": cfg0.h, "top_k": cfg0.top_k,
                    "parallelism": "single GPU"},
-        "roofline": roof,
+        "roofline": head["roofline"],
     }
-    if not args.no_cpu_baseline:
-        n_sample = args.cpu_sample or (16 if decode_like else 8)
-        ref, rows, base = cpu_baseline(layers[0], n_sample, dev)
-        # spot parity of the same tokens on the GPU (layer copy 0)
-        step(0)
-        torch.cuda.synchronize()
-        yg = y[torch.as_tensor(rows, device=dev)].float().cpu().numpy().astype(np.float64)
-        err = np.abs(yg - ref.y).max(axis=1) / np.maximum(np.abs(ref.y).max(axis=1), 1e-6)
-        base["gpu_vs_oracle_max_row_rel_err"] = float(err.max())
-        out["cpu_baseline"] = base
+    if head["cpu_baseline"] is not None:
+        out["cpu_baseline"] = head["cpu_baseline"]
+
+    # the prefill half of the metric: the other benchmark layers in the same run
+    prefill = [int(c) for c in args.prefill.split(",") if c.strip()] if args.prefill else []
+    if prefill:
+        out["prefill"] = {}
+        for pc in prefill:
+            if pc == ci:
+                continue
+            pcfg = W.config(pc)
+            r = measure(pc, args, DEFAULT_STEPS[pc], DEFAULT_WARMUP[pc],
+                        0 if args.no_cpu_baseline else (2 if pcfg.top_k > 1 else 4), 3.0,
+                        with_ceiling=False)
+            entry = {
+                "workload": workload_name(pcfg, args),
+                "steps": r["steps"], "warmup": r["warmup"],
+                "ms_per_step": r["ms_per_step"], "tokens_per_s": r["value"],
+                "layer_TFLOPs": r["detail"]["step_TFLOPs"],
+                "roofline": r["roofline"],
+                "stages_us_per_step": r["detail"]["stages_us_per_step"],
+                "touched_experts": r["detail"]["touched_experts"],
+                "step_hbm_GBps": r["detail"]["step_hbm_GBps"],
+            }
+            if "grouped_down_roofline" in r["detail"]:
+                entry["grouped_down_roofline"] = r["detail"]["grouped_down_roofline"]
+            if r["cpu_baseline"] is not None:
+                entry["cpu_baseline"] = r["cpu_baseline"]
+            out["prefill"][pcfg.name] = entry
+            print(f"[bench] {pcfg.name}: {r['ms_per_step']:.3f} ms/step, "
+                  f"{r['roofline']['kernel']} {r['roofline']['frac']:.3f} of peak",
+                  file=sys.stderr, flush=True)
+    if not args.no_quantizer:
+        detail["quantizer"] = quantizer_leg(dev)
     out["detail"] = detail
     line = json.dumps(out)
     print(line, flush=True)

@@ -90,8 +90,9 @@ int moe_device_check(void);
  * -8, 7), in fp32 with a correctly rounded division.
  *
  *   w       fp32 [rows, K], K % 128 == 0, 16-byte aligned
- *   q       out, uint8 [rows, K/2]: byte j of a row holds code 2j in its low
- *           nibble and code 2j+1 in its high nibble, 4-bit two's complement
+ *   q       out, uint8 [rows, K/2], 16-byte aligned: byte j of a row holds
+ *           code 2j in its low nibble and code 2j+1 in its high nibble, 4-bit
+ *           two's complement
  *   scales  out, fp32 [rows, K/group_size]
  *   group_size  128 (MOE_GROUP_SIZE), 64 or 32
  */
@@ -114,6 +115,23 @@ int moe_quantize_int4_tiled(const float *w, int64_t rows, int64_t K, int32_t gro
                             uint8_t *q, float *scales, void *stream);
 
 /*
+ * Repack one matrix quantized by moe_quantize_int4 (the row-major format of
+ * the quantizer on the discosf.com page, section "FP8 / Int4 混合量化") into
+ * the tiled order moe_forward reads (the layout of moe_quantize_int4_tiled).
+ * Bytes and scales move unchanged, so the result is bit-identical to
+ * moe_quantize_int4_tiled on the same weights.
+ *   q            uint8 [rows, K/2] row-major codes, 16-byte aligned
+ *   scales       fp32 [rows, K/group_size] row-major scales
+ *   rows         multiple of 16; K multiple of 128; group_size 128, 64 or 32
+ *   q_tiled      out, rows*K/2 bytes, 16-byte aligned
+ *   scales_tiled out, rows*K/group_size fp32
+ * The row-major and tiled buffers must not overlap (MOE_ERR_INVALID_ARG).
+ * Asynchronous on `stream`.
+ */
+int moe_tile_int4(const uint8_t *q, const float *scales, int64_t rows, int64_t K,
+                  int32_t group_size, uint8_t *q_tiled, float *scales_tiled, void *stream);
+
+/*
  * Repack a bf16 matrix [rows, K] (rows % 16 == 0, K % 128 == 0) into the
  * tiled order the forward pass reads for the shared expert: tile
  * t = (row/16) * (K/128) + k/128 holds 16 rows x 128 columns as 4 steps of
@@ -133,9 +151,11 @@ typedef struct moe_dims {
     int32_t group_size; /* int4 quantization group: 128, 64 or 32 */
 } moe_dims;
 
-/* Routed experts, each matrix written by moe_quantize_int4_tiled with
- * dims->group_size (g), experts stacked (expert e's matrix starts at e times
- * the matrix size):
+/* Routed experts, each matrix in the TILED int4 layout: written by
+ * moe_quantize_int4_tiled with dims->group_size (g), or by moe_quantize_int4
+ * and then moe_tile_int4. Row-major codes passed here are read as tiles and
+ * give wrong results (the layouts cannot be told apart from the bytes).
+ * Experts are stacked (expert e's matrix starts at e times the matrix size):
  *   w1q, w3q [E] x tiled [h, d]: E*h*d/2 bytes   w1s, w3s: E*h*d/g fp32
  *   w2q      [E] x tiled [d, h]: E*d*h/2 bytes   w2s:      E*d*h/g fp32 */
 typedef struct moe_experts_int4 {

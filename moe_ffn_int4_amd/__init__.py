@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.moe_quantize_int4.restype = ctypes.c_int
         L.moe_quantize_int4_tiled.argtypes = [P, i64, i64, i32, P, P, P]
         L.moe_quantize_int4_tiled.restype = ctypes.c_int
+        L.moe_tile_int4.argtypes = [P, P, i64, i64, i32, P, P, P]
+        L.moe_tile_int4.restype = ctypes.c_int
         L.moe_pack_bf16_tiled.argtypes = [P, i64, i64, P, P]
         L.moe_pack_bf16_tiled.restype = ctypes.c_int
         L.moe_forward_workspace_bytes.argtypes = [ctypes.POINTER(_Dims)]
@@ -192,6 +194,31 @@ def quantize_int4(w: torch.Tensor, q: Optional[torch.Tensor] = None,
     return q, scales
 
 
+def tile_int4(q: torch.Tensor, scales: torch.Tensor, group: int = GROUP,
+              q_tiled: Optional[torch.Tensor] = None,
+              scales_tiled: Optional[torch.Tensor] = None):
+    """Row-major int4 (``quantize_int4`` output: uint8 [rows, K/2] and fp32
+    [rows, K/group]) -> the tiled order the forward pass reads (same shapes)."""
+    _need(q, "q", torch.uint8)
+    _need(scales, "scales", torch.float32)
+    if q.dim() != 2 or scales.dim() != 2:
+        raise ValueError("q and scales must be 2-D")
+    rows, K = q.shape[0], q.shape[1] * 2
+    if tuple(scales.shape) != (rows, K // group):
+        raise ValueError(f"scales has shape {tuple(scales.shape)}, expected {(rows, K // group)}")
+    if q_tiled is None:
+        q_tiled = torch.empty_like(q)
+    if scales_tiled is None:
+        scales_tiled = torch.empty_like(scales)
+    _need(q_tiled, "q_tiled", torch.uint8)
+    _need(scales_tiled, "scales_tiled", torch.float32)
+    if q_tiled.numel() != q.numel() or scales_tiled.numel() != scales.numel():
+        raise ValueError("q_tiled / scales_tiled have the wrong number of elements")
+    _check(lib().moe_tile_int4(_ptr(q), _ptr(scales), rows, K, int(group), _ptr(q_tiled),
+                               _ptr(scales_tiled), _stream(q.device)))
+    return q_tiled, scales_tiled
+
+
 def pack_bf16_tiled(src: torch.Tensor, dst: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bf16 [rows, K] -> the tiled order the forward pass reads (same shape)."""
     _need(src, "src", torch.bfloat16)
@@ -290,6 +317,15 @@ class Int4Experts:
         quantize_int4(w1, self.w1q[e], self.w1s[e], tiled=True, group=g)
         quantize_int4(w3, self.w3q[e], self.w3s[e], tiled=True, group=g)
         quantize_int4(w2, self.w2q[e], self.w2s[e], tiled=True, group=g)
+
+    def set_expert_rowmajor(self, e: int, q1, s1, q3, s3, q2, s2):
+        """Slot ``e`` from row-major int4 (``quantize_int4`` without ``tiled``):
+        W1, W3 codes [h, d/2] and scales [h, d/group], W2 [d, h/2] and [d, h/group],
+        repacked into the tiled order by ``tile_int4``."""
+        g = self.group
+        tile_int4(q1, s1, g, self.w1q[e], self.w1s[e])
+        tile_int4(q3, s3, g, self.w3q[e], self.w3s[e])
+        tile_int4(q2, s2, g, self.w2q[e], self.w2s[e])
 
     def _struct(self) -> _Experts:
         for name in ("w1q", "w3q", "w2q"):

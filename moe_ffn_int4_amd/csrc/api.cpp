@@ -396,7 +396,7 @@ static int quantize(const float* w, int64_t rows, int64_t K, int32_t group_size,
                     (long long)rows);
     if (rows == 0) return MOE_OK;
     CHECK(check_ptr(w, "w"));
-    CHECK(check_ptr(q, "q", tiled ? 16 : 2));
+    CHECK(check_ptr(q, "q"));
     CHECK(check_ptr(scales, "scales", 4));
     CHECK(device_ok());
     HIP_CHECK(moe::launch_quantize_int4(w, rows, K, group_size, q, scales, tiled,
@@ -413,6 +413,37 @@ int moe_quantize_int4(const float* w, int64_t rows, int64_t K, int32_t group_siz
 int moe_quantize_int4_tiled(const float* w, int64_t rows, int64_t K, int32_t group_size, uint8_t* q,
                             float* scales, void* stream) {
     return quantize(w, rows, K, group_size, q, scales, true, stream);
+}
+
+int moe_tile_int4(const uint8_t* q, const float* scales, int64_t rows, int64_t K, int32_t group_size,
+                  uint8_t* q_tiled, float* scales_tiled, void* stream) {
+    g_last_error.clear();
+    if (!group_ok(group_size))
+        return fail(MOE_ERR_INVALID_ARG, "group_size %d unsupported (128, 64 or 32)", group_size);
+    if (rows < 0 || rows % 16)
+        return fail(MOE_ERR_INVALID_ARG, "rows = %lld must be a non-negative multiple of 16",
+                    (long long)rows);
+    if (K < 128 || K % 128)
+        return fail(MOE_ERR_INVALID_ARG, "K = %lld must be a positive multiple of 128", (long long)K);
+    if (rows == 0) return MOE_OK;
+    CHECK(check_ptr(q, "q"));
+    CHECK(check_ptr(scales, "scales", 4));
+    CHECK(check_ptr(q_tiled, "q_tiled"));
+    CHECK(check_ptr(scales_tiled, "scales_tiled", 4));
+    auto overlap = [](const void* a, const void* b, uintptr_t n, uintptr_t m) {
+        const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+        return x < y + m && y < x + n;
+    };
+    const uintptr_t nq = static_cast<uintptr_t>(rows) * (K / 2);
+    const uintptr_t ns = static_cast<uintptr_t>(rows) * (K / group_size) * 4;
+    if (overlap(q, q_tiled, nq, nq) || overlap(q, scales_tiled, nq, ns) ||
+        overlap(scales, q_tiled, ns, nq) || overlap(scales, scales_tiled, ns, ns))
+        return fail(MOE_ERR_INVALID_ARG, "the row-major and tiled buffers overlap");
+    CHECK(device_ok());
+    HIP_CHECK(moe::launch_tile_int4(q, scales, rows, K, group_size, q_tiled, scales_tiled,
+                                    static_cast<hipStream_t>(stream)),
+              "tile launch");
+    return MOE_OK;
 }
 
 int moe_pack_bf16_tiled(const uint16_t* src, int64_t rows, int64_t K, uint16_t* dst, void* stream) {

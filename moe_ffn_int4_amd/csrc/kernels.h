@@ -55,6 +55,10 @@ constexpr int kSmallRoutePairs = 1024;
 // group: 128, 64 or 32 weights per scale; K % 128 == 0
 hipError_t launch_quantize_int4(const float* w, int64_t rows, int64_t K, int group, uint8_t* q,
                                 float* scales, bool tiled, hipStream_t stream);
+// row-major int4 codes [rows, K/2] + scales [rows, K/group] -> the tiled order
+// (rows % 16 == 0)
+hipError_t launch_tile_int4(const uint8_t* q_rm, const float* s_rm, int64_t rows, int64_t K, int group,
+                            uint8_t* q_t, float* s_t, hipStream_t stream);
 // fp8 (E4M3) row-wise quantization: weights fp32 [rows, K] -> tiled codes
 // (16 x 128 tiles of 4 steps x 16 rows x 32 bytes) + per-row scales;
 // activations bf16 [rows, K] -> row-major codes + per-row scales (ub > 0

@@ -6,87 +6,156 @@
 // smaller groups the lshu.cn page expects next), scale = max(max|w|, 1e-6) / 8
 // and code = clamp(round_half_even(w / scale), -8, 7).
 //
-// Bound by HBM: 4 bytes read and 0.5 + 4/128 bytes written per weight.
-// Mapping: one half-wave (32 lanes) per 128 weights of a row, each lane one
-// float4, so a wave reads 1 KB in one fully coalesced load and writes 2 x 64
-// bytes of packed codes. A group's max is an xor-shuffle reduction over its
+// Bound by HBM: 4 bytes read and 0.5 + 4/group bytes written per weight.
+// Mapping: one wave per 16-row x 128-column tile of w (8 KB of fp32), all of
+// it requested at once: load i brings rows 2i and 2i+1 (two whole 512-byte
+// row segments, one float4 per lane), so lane l holds columns 4(l%32) .. +3
+// of rows 2i + l/32. A group's max is an xor-shuffle reduction over its
 // group / 4 lanes (5 steps for 128, 4 for 64, 3 for 32). The division is IEEE
 // correctly rounded (the library is compiled with
 // -fhip-fp32-correctly-rounded-divide-sqrt and no fast-math), rintf maps to
 // round-half-even, so codes and scales are bit-identical to the fp32
-// definition.
+// definition. The tile's codes (1 KB) and scales gather in LDS, and each lane
+// then stores one whole 16-byte piece, so every output line is written once,
+// in full.
 //
 // TILED = true writes the storage order the forward pass reads: tile
 // t = (row/16) * (K/128) + k/128 holds those 128 columns of 16 rows (1 KB) as
 // four 32-column steps of 16 rows x 16 bytes, and their 16 x (128 / group)
 // scales, scale s of row r at t*16*S + (r%16)*S + s (S = 128 / group): one
 // wavefront access covers one tile, one GEMM step of 16 rows is 256
-// contiguous bytes.
+// contiguous bytes. Row-major output: row r's 128 columns of tile column g are
+// bytes r*K/2 + 64 g .. + 63.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-template <bool TILED>
-__global__ __launch_bounds__(256) void quantize_int4_kernel(const float4* __restrict__ w,
-                                                            int64_t ngroups, int64_t groups_per_row,
-                                                            int group, uint16_t* __restrict__ q16,
-                                                            float* __restrict__ scales) {
-    // ngroups / groups_per_row count 128-weight units; a unit holds S groups
-    const int lane = threadIdx.x & 63;
-    const int half = lane >> 5;
-    const int hl = lane & 31;
-    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-    const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+namespace {
+constexpr int kQuantWaves = 4;  // waves (tiles in flight) per block
+}
 
-    for (int64_t g0 = wave * 2; g0 < ngroups; g0 += nwaves * 2) {
-        const int64_t g = g0 + half;
-        const bool valid = g < ngroups;
-        float4 v = valid ? w[g * 32 + hl] : make_float4(0.f, 0.f, 0.f, 0.f);
-        float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        for (int off = group >> 3; off >= 1; off >>= 1) {  // lanes of one group
-            float o = __shfl_xor(m, off, 64);
-            m = o > m ? o : m;
-        }
-        const float s = (m < 1e-6f ? 1e-6f : m) / 8.0f;
-        float e[4] = {v.x, v.y, v.z, v.w};
-        uint32_t packed = 0;
+template <bool TILED>
+__global__ __launch_bounds__(256) void quantize_int4_kernel(const float* __restrict__ w, int64_t rows,
+                                                            int64_t K, int group,
+                                                            uint8_t* __restrict__ q,
+                                                            float* __restrict__ scales) {
+    // per wave: the tile's codes in tiled order (step s, row r at s*256 + r*16)
+    // and its 16 x S scales
+    __shared__ __attribute__((aligned(16))) uint8_t code_lds[kQuantWaves][1024];
+    __shared__ float scale_lds[kQuantWaves][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int half = lane >> 5, c4 = lane & 31;
+    const int64_t ng = K / kGroup;
+    const int64_t ntiles = (rows + 15) / 16 * ng;
+    const int S = kGroup / group, lanes = group >> 2;
+    // every wave of a block runs the same iterations (block-wide barriers)
+    for (int64_t tb = static_cast<int64_t>(blockIdx.x) * kQuantWaves; tb < ntiles;
+         tb += static_cast<int64_t>(gridDim.x) * kQuantWaves) {
+        const int64_t t = tb + wv;
+        const bool tv = t < ntiles;
+        const int64_t rb = tv ? t / ng : 0, g = tv ? t - rb * ng : 0;
+        f32x4 v[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float c = rintf(e[i] / s);
-            c = c < -8.0f ? -8.0f : (c > 7.0f ? 7.0f : c);
-            packed |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xFu) << (4 * i);
+        for (int i = 0; i < 8; ++i) {
+            const int64_t row = rb * 16 + 2 * i + half;
+            v[i] = (tv && row < rows)
+                       ? __builtin_nontemporal_load(
+                             reinterpret_cast<const f32x4*>(w + row * K + g * kGroup + c4 * 4))
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (valid) {
-            int64_t at = g;  // row-major: unit g of the flattened [rows, K/128]
-            if (TILED) {
-                const int64_t r = g / groups_per_row, gg = g - r * groups_per_row;
-                at = ((r >> 4) * groups_per_row + gg) * 16 + (r & 15);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 2 * i + half;
+            float m = fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3])));
+            for (int off = group >> 3; off >= 1; off >>= 1) {  // the lanes of one group
+                const float o = __shfl_xor(m, off, 64);
+                m = o > m ? o : m;
             }
-            // tiled: 32-column step (hl / 8) of the 16-row tile, then the row, then
-            // this lane's 4 codes; row-major: the row's 64 bytes in order
-            q16[TILED ? (at >> 4) * 512 + (hl >> 3) * 128 + (at & 15) * 8 + (hl & 7) : at * 32 + hl] =
+            const float s = (m < 1e-6f ? 1e-6f : m) / 8.0f;
+            uint32_t packed = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float c = rintf(v[i][j] / s);
+                c = c < -8.0f ? -8.0f : (c > 7.0f ? 7.0f : c);
+                packed |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xFu) << (4 * j);
+            }
+            // columns 4 c4 .. 4 c4 + 3 sit in step c4 / 8, bytes 2 (c4 % 8) .. + 1
+            *reinterpret_cast<uint16_t*>(&code_lds[wv][(c4 >> 3) * 256 + r * 16 + (c4 & 7) * 2]) =
                 static_cast<uint16_t>(packed);
-            const int lanes = group >> 2, S = kGroup / group;
-            if (hl % lanes == 0) scales[at * S + hl / lanes] = s;
+            if (c4 % lanes == 0) scale_lds[wv][r * S + c4 / lanes] = s;
         }
+        __syncthreads();
+        if (tv) {
+            if (TILED) {
+                // lane l: step l / 16, row l % 16 -- the tile's 1 KB in order
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&code_lds[wv][lane * 16]),
+                                            reinterpret_cast<u32x4*>(q + t * 1024 + lane * 16));
+                if (lane < 16 * S) scales[t * 16 * S + lane] = scale_lds[wv][lane];
+            } else {
+                // lane l: row l / 4, columns 32 (l % 4) .. + 31 of the tile
+                const int r = lane >> 2, p = lane & 3;
+                const int64_t row = rb * 16 + r;
+                if (row < rows)
+                    __builtin_nontemporal_store(
+                        *reinterpret_cast<const u32x4*>(&code_lds[wv][p * 256 + r * 16]),
+                        reinterpret_cast<u32x4*>(q + row * (K / 2) + g * 64 + p * 16));
+                if (lane < 16 * S) {
+                    const int64_t srow = rb * 16 + lane / S;
+                    if (srow < rows) scales[srow * (K / group) + g * S + lane % S] = scale_lds[wv][lane];
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
 hipError_t launch_quantize_int4(const float* w, int64_t rows, int64_t K, int group, uint8_t* q,
                                 float* scales, bool tiled, hipStream_t stream) {
-    const int64_t ngroups = rows * (K / kGroup);
-    if (ngroups == 0) return hipSuccess;
-    const int64_t want = (ngroups + 7) / 8;  // 8 units per 256-thread block per pass
-    const int blocks = static_cast<int>(want < 8192 ? want : 8192);
+    const int64_t ntiles = (rows + 15) / 16 * (K / kGroup);
+    if (ntiles == 0) return hipSuccess;
+    const int64_t want = (ntiles + kQuantWaves - 1) / kQuantWaves;
+    const int blocks = static_cast<int>(want < 16384 ? want : 16384);
     if (tiled)
-        MOE_LAUNCH(quantize_int4_kernel<true>, dim3(blocks), dim3(256), 0, stream,
-                           reinterpret_cast<const float4*>(w), ngroups, K / kGroup, group,
-                           reinterpret_cast<uint16_t*>(q), scales);
+        MOE_LAUNCH(quantize_int4_kernel<true>, dim3(blocks), dim3(256), 0, stream, w, rows, K, group,
+                   q, scales);
     else
-        MOE_LAUNCH(quantize_int4_kernel<false>, dim3(blocks), dim3(256), 0, stream,
-                           reinterpret_cast<const float4*>(w), ngroups, K / kGroup, group,
-                           reinterpret_cast<uint16_t*>(q), scales);
+        MOE_LAUNCH(quantize_int4_kernel<false>, dim3(blocks), dim3(256), 0, stream, w, rows, K, group,
+                   q, scales);
+    return hipGetLastError();
+}
+
+// Row-major int4 (the quantizer's row-major output) -> the tiled order, one
+// wave per tile: lane l moves the 16-byte piece of step l / 16, row l % 16
+// (bytes 64 g + 16 (l / 16) .. of the row) to byte 16 l of the tile, and
+// lanes below 16 S move the tile's scales.
+__global__ __launch_bounds__(256) void tile_int4_kernel(const uint8_t* __restrict__ q_rm,
+                                                        const float* __restrict__ s_rm, int64_t rows,
+                                                        int64_t K, int group, uint8_t* __restrict__ q_t,
+                                                        float* __restrict__ s_t) {
+    const int lane = threadIdx.x & 63;
+    const int64_t ng = K / kGroup;
+    const int64_t ntiles = rows / 16 * ng;
+    const int S = kGroup / group;
+    for (int64_t t = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6; t < ntiles;
+         t += (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6) {
+        const int64_t rb = t / ng, g = t - rb * ng;
+        const int64_t row = rb * 16 + (lane & 15);
+        const u32x4 v = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(q_rm + row * (K / 2) + g * 64 + (lane >> 4) * 16));
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(q_t + t * 1024 + lane * 16));
+        if (lane < 16 * S)
+            s_t[t * 16 * S + lane] = s_rm[(rb * 16 + lane / S) * (K / group) + g * S + lane % S];
+    }
+}
+
+hipError_t launch_tile_int4(const uint8_t* q_rm, const float* s_rm, int64_t rows, int64_t K, int group,
+                            uint8_t* q_t, float* s_t, hipStream_t stream) {
+    const int64_t ntiles = rows / 16 * (K / kGroup);
+    if (ntiles == 0) return hipSuccess;
+    const int64_t want = (ntiles + 3) / 4;
+    const int blocks = static_cast<int>(want < 16384 ? want : 16384);
+    MOE_LAUNCH(tile_int4_kernel, dim3(blocks), dim3(256), 0, stream, q_rm, s_rm, rows, K, group, q_t, s_t);
     return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for need in ("moe_quantize_int4", "moe_quantize_int4_tiled", "moe_pack_bf16_tiled",
+    for need in ("moe_quantize_int4", "moe_quantize_int4_tiled", "moe_tile_int4", "moe_pack_bf16_tiled",
                  "moe_forward", "moe_forward_path", "moe_route",
                  "moe_forward_workspace_bytes", "moe_route_workspace_bytes",
                  "moe_status_string", "moe_last_error", "moe_abi_version", "moe_device_check"):
@@ -146,7 +146,27 @@ def test_quantize_validation(L):
     assert L.moe_quantize_int4(None, 4, 256, 128, FAKE, FAKE, None) == INVALID
     assert L.moe_quantize_int4(FAKE, 4, 256, 128, None, FAKE, None) == INVALID
     assert L.moe_quantize_int4(FAKE, 4, 256, 128, FAKE, FAKE + 1, None) == INVALID
+    assert L.moe_quantize_int4(FAKE, 4, 256, 128, FAKE + 8, FAKE, None) == INVALID  # q 16-byte aligned
+    assert "aligned" in L.moe_last_error().decode()
     assert L.moe_quantize_int4(FAKE, 0, 256, 128, FAKE, FAKE, None) == OK  # nothing to do
+
+
+def test_tile_int4_validation(L):
+    A, B, C, D = FAKE, FAKE * 64, FAKE * 128, FAKE * 192  # far apart: no overlap
+    assert L.moe_tile_int4(A, B, 20, 256, 128, C, D, None) == INVALID
+    assert "multiple of 16" in L.moe_last_error().decode()
+    assert L.moe_tile_int4(A, B, 32, 200, 128, C, D, None) == INVALID
+    assert L.moe_tile_int4(A, B, 32, 256, 16, C, D, None) == INVALID
+    assert "group_size" in L.moe_last_error().decode()
+    assert L.moe_tile_int4(None, B, 32, 256, 128, C, D, None) == INVALID
+    assert L.moe_tile_int4(A + 8, B, 32, 256, 128, C, D, None) == INVALID
+    assert L.moe_tile_int4(A, B + 2, 32, 256, 128, C, D, None) == INVALID
+    assert L.moe_tile_int4(A, B, 32, 256, 128, None, D, None) == INVALID
+    # 32 rows x 256 columns: 4 KB of codes; a tiled copy 1 KB further overlaps
+    assert L.moe_tile_int4(A, B, 32, 256, 128, A + 1024, D, None) == INVALID
+    assert "overlap" in L.moe_last_error().decode()
+    assert L.moe_tile_int4(A, B, 32, 256, 128, C, B + 16, None) == INVALID
+    assert L.moe_tile_int4(A, B, 0, 256, 128, C, D, None) == OK  # nothing to do
 
 
 def test_tiled_quantize_and_pack_validation(L):

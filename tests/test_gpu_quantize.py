@@ -117,3 +117,55 @@ def test_pack_bf16_tiled(rows, K):
         t = (r // 16) * (K // 128) + k // 128
         at = t * 2048 + ((k % 128) // 32) * 512 + (r % 16) * 32 + (k % 32)
         assert flat[at] == ref[r, k]
+
+
+@pytest.mark.parametrize("group", [128, 64, 32])
+@pytest.mark.parametrize("rows,K", [(16, 128), (48, 384), (8192, 5120)])
+def test_tile_int4_equals_tiled_quantizer(rows, K, group):
+    """moe_quantize_int4 then moe_tile_int4 gives the bytes of moe_quantize_int4_tiled."""
+    say(f"tile int4: rows={rows} K={K} group={group}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(rows * 31 + K + group)
+    w = torch.randn(rows, K, device=DEV, generator=g) * 0.02
+    w[1::9] *= 1e-5
+    q_rm, s_rm = moe.quantize_int4(w, group=group)
+    q_t, s_t = moe.tile_int4(q_rm, s_rm, group)
+    q_ref, s_ref = moe.quantize_int4(w, tiled=True, group=group)
+    torch.cuda.synchronize()
+    assert torch.equal(q_t, q_ref)
+    assert torch.equal(s_t.view(torch.int32), s_ref.view(torch.int32))
+
+
+def _experts_two_ways(cfg, group=128):
+    """The layer's routed experts quantized row-major and repacked, and tiled directly."""
+    a = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, DEV, group)
+    b = moe.Int4Experts.empty(cfg.E, cfg.d, cfg.h, DEV, group)
+    for e in range(cfg.E):
+        ws = [W.gen_expert_weight(cfg, n, e, DEV) for n in ("w1", "w3", "w2")]
+        parts = []
+        for w in ws:
+            parts.extend(moe.quantize_int4(w, group=group))
+        a.set_expert_rowmajor(e, *parts)
+        b.quantize_expert(e, *ws)
+    torch.cuda.synchronize()
+    return a, b
+
+
+@pytest.mark.parametrize("i,group", [(0, 128), (0, 32), (1, 128), (2, 128)])
+def test_rowmajor_quantizer_feeds_the_forward(i, group):
+    """moe_quantize_int4 -> moe_tile_int4 -> moe_forward equals
+    moe_quantize_int4_tiled -> moe_forward bit for bit."""
+    cfg = W.config(i)
+    say(f"row-major experts through moe_tile_int4: config {i} ({cfg.name}) group {group}")
+    a, b = _experts_two_ways(cfg, group)
+    for name in ("w1q", "w3q", "w2q", "w1s", "w3s", "w2s"):
+        assert torch.equal(getattr(a, name).view(torch.uint8), getattr(b, name).view(torch.uint8)), name
+    x = W.gen_x(cfg).to(DEV)
+    wr, bias = W.gen_router(cfg)
+    wr = wr.to(DEV)
+    bias = None if bias is None else bias.to(DEV)
+    shared = moe.pack_shared(*(s.to(DEV) for s in W.gen_shared(cfg, DEV)))
+    ya = moe.forward(x, wr, bias, a, shared, cfg.top_k)
+    yb = moe.forward(x, wr, bias, b, shared, cfg.top_k)
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
