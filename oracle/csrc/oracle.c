@@ -313,6 +313,18 @@ static double bf16_round_value(double v)
     return (double)f;
 }
 
+/* oracle_fp8_value of every code, filled once before the parallel loops
+ * (a lookup of the same values, so the products below are unchanged) */
+static double fp8_value_table[256];
+static int fp8_value_table_ready;
+
+static void fp8_table_init(void)
+{
+    if (fp8_value_table_ready) return;
+    for (int c = 0; c < 256; ++c) fp8_value_table[c] = oracle_fp8_value((uint8_t)c);
+    fp8_value_table_ready = 1;
+}
+
 /* bf16(sum_j fp8(a[j]) fp8(w[row][j]) * sa * sw[row]): the products are exact
  * and so is their fp64 sum (every term is a multiple of 2^-18 below 2^18) */
 static double fp8_row_product(const uint8_t *a, float sa, const uint8_t *w, const float *sw,
@@ -320,7 +332,7 @@ static double fp8_row_product(const uint8_t *a, float sa, const uint8_t *w, cons
 {
     double acc = 0.0;
     for (int64_t j = 0; j < K; ++j)
-        acc += oracle_fp8_value(a[j]) * oracle_fp8_value(w[row * K + j]);
+        acc += fp8_value_table[a[j]] * fp8_value_table[w[row * K + j]];
     return bf16_round_value(acc * (double)sa * (double)sw[row]);
 }
 
@@ -335,6 +347,7 @@ void oracle_swiglu_fp8_token(const double *x, int64_t d, int64_t h,
                              float *f32, uint8_t *codes, double *u, double *o)
 {
     float sx, su;
+    fp8_table_init();
     for (int64_t j = 0; j < d; ++j) f32[j] = (float)x[j];
     quantize_fp8_row(f32, d, ub, codes, &sx);
     #pragma omp parallel for schedule(static)

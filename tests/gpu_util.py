@@ -16,7 +16,7 @@ import torch
 import moe_ffn_int4_amd as moe
 import workloads as W
 from oracle import native
-from oracle.moe import Bf16Expert, Int4Expert
+from oracle.moe import Bf16Expert, Int4Expert, MoEResult
 
 TOL = 2e-2  # max relative error of an output row (infinity norm)
 MARGIN = 1e-4  # top-k margin above which expert ids must match exactly
@@ -126,10 +126,17 @@ def oracle_forward_rows(layer: Layer, rows: np.ndarray, gpu_ids: Optional[np.nda
         experts[e] = oracle_expert(layer, e)
         if len(need) > 16 and (i + 1) % 32 == 0:
             say(f"  oracle: {i + 1}/{len(need)} experts quantized")
-    if len(rows) > 64:
-        say(f"  oracle: per-token loop over {len(rows)} tokens")
-    r = native.moe_forward_per_token(xs, layer.wr.numpy(), b, cfg.top_k, experts, layer.shared,
-                                     forced_ids=forced, group_size=layer.group)
+    # the per-token loop in batches of tokens, reporting progress between them
+    batch = 32
+    parts = []
+    for i in range(0, len(rows), batch):
+        parts.append(native.moe_forward_per_token(
+            xs[i:i + batch], layer.wr.numpy(), b, cfg.top_k, experts, layer.shared,
+            forced_ids=None if forced is None else forced[i:i + batch], group_size=layer.group))
+        if len(rows) > batch:
+            say(f"  oracle: {min(i + batch, len(rows))}/{len(rows)} tokens")
+    r = MoEResult(*(np.concatenate([getattr(p, f) for p in parts])
+                    for f in ("y", "ids", "gates", "logits", "margin")))
     return r, margin
 
 
