@@ -203,6 +203,29 @@ int moe_forward_path(const moe_dims *dims, const uint16_t *x, const float *route
                      float *topk_gates, int32_t path, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/*
+ * moe_forward_path without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library (each GPU the library runs on
+ * holds its own copy until the process ends); nothing is allocated or freed by
+ * a call. Layers whose moe_forward_workspace_bytes(dims) exceed it return
+ * MOE_ERR_WORKSPACE (64 MiB holds, e.g., up to about 550 tokens at top-1 with
+ * d = 5120, h = 8192).
+ * The first call on a device does a one-time set-up there (the array's device
+ * address and the library's second stream for the hybrid path); make it
+ * outside graph capture. Every call on a GPU shares that GPU's array and
+ * leaves its contents behind: calls that overlap on one GPU (different
+ * streams, or host threads) race on it and must be serialised by the caller.
+ * Stage timing (moe_profile_enable) creates events; keep it off here.
+ * Arguments, outputs, paths and errors otherwise as moe_forward_path.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const moe_dims *dims, const uint16_t *x, const float *router_w,
+                        const float *router_b, const moe_experts_int4 *experts,
+                        const moe_shared_bf16 *shared, uint16_t *y, int32_t *topk_ids,
+                        float *topk_gates, int32_t path, void *stream);
+
 /* Row-wise fp8 (OCP E4M3) quantization of the fp8 routed-expert path: the
  * lshu.cn page (section "量化环节") quantizes each activation row to fp8 with
  * its scale bounded by activation_scale_ub, and holds the weights in fp8 with

@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.restype = ctypes.c_int
         L.moe_forward_path.argtypes = fwd + [i32, P, sz, P]
         L.moe_forward_path.restype = ctypes.c_int
+        L.moe_forward_noalloc.argtypes = fwd + [i32, P]
+        L.moe_forward_noalloc.restype = ctypes.c_int
         fwd_bf16 = list(fwd)
         fwd_bf16[4] = ctypes.POINTER(_ExpertsBf16)
         L.moe_forward_bf16.argtypes = fwd_bf16 + [i32, P, sz, P]
@@ -494,6 +496,45 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Te
         ctypes.byref(sh), _ptr(y), _ptr(topk_ids), _ptr(topk_gates), PATHS[path],
         _ptr(workspace), workspace.numel(), _stream(x.device)))
     return y
+
+
+def forward_noalloc(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor],
+                    experts: "Int4Experts", shared, top_k: int, path: str = "auto",
+                    y: Optional[torch.Tensor] = None, topk_ids: Optional[torch.Tensor] = None,
+                    topk_gates: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``forward`` for int4 experts through the allocation-free entry point: its
+    workspace is the library's static device scratch (NOALLOC_SCRATCH_BYTES),
+    shared by every such call on the GPU, so overlapping calls race."""
+    _need(x, "x", torch.bfloat16)
+    T, d = x.shape
+    E, h = router_w.shape[0], experts.h
+    _need(router_w, "router_w", torch.float32, (E, d))
+    if router_b is not None:
+        _need(router_b, "router_b", torch.float32, (E,))
+    s1, s3, s2 = shared
+    _need(s1, "S1", torch.bfloat16, (h, d))
+    _need(s3, "S3", torch.bfloat16, (h, d))
+    _need(s2, "S2", torch.bfloat16, (d, h))
+    if not isinstance(experts, Int4Experts) or experts.E != E or experts.d != d:
+        raise ValueError("experts must be Int4Experts matching the router / x")
+    if y is None:
+        y = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16, (T, d))
+    if topk_ids is not None:
+        _need(topk_ids, "topk_ids", torch.int32, (T, top_k))
+    if topk_gates is not None:
+        _need(topk_gates, "topk_gates", torch.float32, (T, top_k))
+    dims = _dims(T, d, E, h, top_k, experts.group)
+    ex = experts._struct()
+    sh = _Shared(s1.data_ptr(), s3.data_ptr(), s2.data_ptr())
+    _check(lib().moe_forward_noalloc(
+        ctypes.byref(dims), _ptr(x), _ptr(router_w), _ptr(router_b), ctypes.byref(ex),
+        ctypes.byref(sh), _ptr(y), _ptr(topk_ids), _ptr(topk_gates), PATHS[path],
+        _stream(x.device)))
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def route(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor],

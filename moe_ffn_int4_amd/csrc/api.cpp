@@ -332,6 +332,37 @@ int side_stream(Side** out) {
     return MOE_OK;
 }
 
+// ---- scratch of the allocation-free forward (moe_forward_noalloc)
+// Its workspace is this file-scope device array: every GPU the library runs on
+// holds its own copy, at its own address, until the process ends. In host code
+// the array's name is a host-side stand-in, not a device address: host code
+// only ever uses the address hipGetSymbolAddress returns for the current
+// device (scratch_address), never the name.
+constexpr size_t kScratchBytes = static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Set-up, once per device with that device current: the array's device address,
+// and the hybrid path's second stream, so later calls create nothing.
+int scratch_address(void** out) {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    HIP_CHECK(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED_DEVICE, "device ordinal %d", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (!p || !aligned(p, kAlign))
+            return fail(MOE_ERR_HIP, "scratch has no 256-byte aligned device address");
+        Side* side = nullptr;
+        CHECK(side_stream(&side));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return MOE_OK;
+}
+
 // Router partial logits, then either the one-block small-batch finish (top-k,
 // dispatch, decode chunks) or the top-k kernel + the per-expert dispatch kernel.
 // small_rows: which groups get streaming chunks and which GEMM tiles (build_work_lists)
@@ -876,6 +907,26 @@ int moe_forward(const moe_dims* dims, const uint16_t* x, const float* router_w,
                 void* workspace, size_t workspace_bytes, void* stream) {
     return moe_forward_path(dims, x, router_w, router_b, experts, shared, y, topk_ids, topk_gates,
                             MOE_PATH_AUTO, workspace, workspace_bytes, stream);
+}
+
+int moe_forward_noalloc(const moe_dims* dims, const uint16_t* x, const float* router_w,
+                        const float* router_b, const moe_experts_int4* experts,
+                        const moe_shared_bf16* shared, uint16_t* y, int32_t* topk_ids,
+                        float* topk_gates, int32_t path, void* stream) {
+    g_last_error.clear();
+    CHECK(check_dims(dims));
+    if (!experts) return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
+    const size_t need = layout(*dims).total;
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_WORKSPACE,
+                    "the layer needs %zu bytes of workspace; the allocation-free forward has %zu "
+                    "(MOE_NOALLOC_SCRATCH_BYTES): use moe_forward_path with a workspace",
+                    need, kScratchBytes);
+    CHECK(device_ok());
+    void* ws = nullptr;
+    CHECK(scratch_address(&ws));
+    return forward_impl(dims, x, router_w, router_b, experts, nullptr, nullptr, shared, y, topk_ids,
+                        topk_gates, path, ws, kScratchBytes, stream);
 }
 
 static int stream_args(const void* a, const void* b, int64_t bytes) {

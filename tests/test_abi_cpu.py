@@ -279,3 +279,21 @@ def test_binding_group_sizes():
     assert s.shape == (32, 4)
     # row 17, group 3: tile (1, 1), row 1, scale 1 of that tile -> ((1*2+1)*16 + 1)*2 + 1
     assert s[17, 3].item() == ((1 * 2 + 1) * 16 + 1) * 2 + 1
+
+
+def test_noalloc_validation(L):
+    """moe_forward_noalloc refuses bad dims and layers past its scratch before any HIP call."""
+    ex = ctypes.byref(moe._Experts(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE))
+    sh = ctypes.byref(moe._Shared(FAKE, FAKE, FAKE))
+    bad = _dims(T=0)
+    assert L.moe_forward_noalloc(ctypes.byref(bad), FAKE, FAKE, None, ex, sh, FAKE, None, None,
+                                 0, None) == INVALID
+    assert L.moe_forward_noalloc(ctypes.byref(_dims()), FAKE, FAKE, None, None, sh, FAKE, None,
+                                 None, 0, None) == INVALID
+    big = moe._Dims(8192, 5120, 16, 8192, 1, 128)
+    assert L.moe_forward_workspace_bytes(ctypes.byref(big)) > moe.NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(ctypes.byref(big), FAKE, FAKE, None, ex, sh, FAKE, None, None,
+                                 0, None) == WORKSPACE
+    assert "MOE_NOALLOC_SCRATCH_BYTES" in L.moe_last_error().decode()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)" in open(HEADER).read()
+    assert moe.NOALLOC_SCRATCH_BYTES == 64 << 20
