@@ -11,11 +11,13 @@
 // it requested at once: load i brings rows 2i and 2i+1 (two whole 512-byte
 // row segments, one float4 per lane), so lane l holds columns 4(l%32) .. +3
 // of rows 2i + l/32. A group's max is an xor-shuffle reduction over its
-// group / 4 lanes (5 steps for 128, 4 for 64, 3 for 32). The division is IEEE
-// correctly rounded (the library is compiled with
-// -fhip-fp32-correctly-rounded-divide-sqrt and no fast-math), rintf maps to
-// round-half-even, so codes and scales are bit-identical to the fp32
-// definition. The tile's codes (1 KB) and scales gather in LDS, and each lane
+// group / 4 lanes (5 steps for 128, 4 for 64, 3 for 32). The codes round the
+// IEEE correctly rounded quotient (the library is compiled with
+// -fhip-fp32-correctly-rounded-divide-sqrt and no fast-math) half to even
+// (rintf): each weight is first multiplied by the scale's approximate
+// reciprocal, and only a product near a rounding boundary takes the IEEE
+// division, so codes and scales are bit-identical to the fp32 definition at
+// a fraction of the division's VALU cost. The tile's codes (1 KB) and scales gather in LDS, and each lane
 // then stores one whole 16-byte piece, so every output line is written once,
 // in full.
 //
@@ -33,6 +35,9 @@ namespace moe {
 
 namespace {
 constexpr int kQuantWaves = 4;  // waves (tiles in flight) per block
+// distance to a rounding boundary below which the quotient is computed
+// exactly: 8 ulp of 8.0 (v_rcp_f32 is within 1 ulp, the product adds 1/2)
+constexpr float kNearHalf = 8.0f * 9.5367431640625e-7f;
 }
 
 template <bool TILED>
@@ -73,10 +78,18 @@ __global__ __launch_bounds__(256) void quantize_int4_kernel(const float* __restr
                 m = o > m ? o : m;
             }
             const float s = (m < 1e-6f ? 1e-6f : m) / 8.0f;
+            const float rs = __builtin_amdgcn_rcpf(s);
             uint32_t packed = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float c = rintf(v[i][j] / s);
+                // round(w / s): the product with the approximate reciprocal is
+                // within 3 ulp of w / s (|w / s| <= 8), so its rounding agrees
+                // with that of the correctly rounded quotient unless it lies
+                // within kNearHalf of a rounding boundary n + 1/2; there the
+                // IEEE division decides
+                const float qa = v[i][j] * rs;
+                float c = rintf(qa);
+                if (fabsf(fabsf(qa - c) - 0.5f) < kNearHalf) c = rintf(v[i][j] / s);
                 c = c < -8.0f ? -8.0f : (c > 7.0f ? 7.0f : c);
                 packed |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xFu) << (4 * j);
             }

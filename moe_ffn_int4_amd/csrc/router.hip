@@ -25,11 +25,9 @@
 
 namespace moe {
 
-namespace {
-constexpr int RK = 32;  // reduction chunk staged in LDS
-}  // namespace
-
-template <int TT, int EE, int MT, int ME>
+// RK: reduction chunk staged in LDS. The decode tile (16 x 16) stages its
+// whole 128-column slice at once, so its loads take one memory round trip.
+template <int TT, int EE, int MT, int ME, int RK = 32>
 __global__ __launch_bounds__(256) void router_partials_kernel(const uint16_t* __restrict__ x,
                                                               const float* __restrict__ wr,
                                                               int64_t T, int64_t d, int64_t E,
@@ -48,8 +46,66 @@ __global__ __launch_bounds__(256) void router_partials_kernel(const uint16_t* __
     const int ee = tid % EW;     // experts ee + EW*j
     float acc[MT][ME] = {};
 
+    // every load of a chunk is issued before its LDS stores
+    constexpr int XN = TT * (RK / 4), WN = EE * (RK / 4);
+    constexpr int XI = (XN + 255) / 256, WI = (WN + 255) / 256;
+    for (int64_t k0 = kb; k0 < kb + slice; k0 += RK) {
+        uint2 xv[XI];
+        float4 wv[WI];
+#pragma unroll
+        for (int i = 0; i < XI; ++i) {  // x: TT x RK bf16
+            const int idx = tid + 256 * i;
+            const int r = idx / (RK / 4), c = (idx % (RK / 4)) * 4;
+            const int64_t t = t0 + r;
+            xv[i] = (idx < XN && t < T) ? *reinterpret_cast<const uint2*>(x + t * d + k0 + c)
+                                        : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < WI; ++i) {  // router: EE x RK fp32
+            const int idx = tid + 256 * i;
+            const int r = idx / (RK / 4), c = (idx % (RK / 4)) * 4;
+            const int64_t e = e0 + r;
+            wv[i] = (idx < WN && e < E) ? *reinterpret_cast<const float4*>(wr + e * d + k0 + c)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < XI; ++i) {
+            const int idx = tid + 256 * i;
+            if (idx >= XN) continue;
+            const int r = idx / (RK / 4), c = (idx % (RK / 4)) * 4;
+            xs[r][c + 0] = __uint_as_float(xv[i].x << 16);
+            xs[r][c + 1] = __uint_as_float(xv[i].x & 0xFFFF0000u);
+            xs[r][c + 2] = __uint_as_float(xv[i].y << 16);
+            xs[r][c + 3] = __uint_as_float(xv[i].y & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < WI; ++i) {
+            const int idx = tid + 256 * i;
+            if (idx >= WN) continue;
+            const int r = idx / (RK / 4), c = (idx % (RK / 4)) * 4;
+            ws[r][c + 0] = wv[i].x;
+            ws[r][c + 1] = wv[i].y;
+            ws[r][c + 2] = wv[i].z;
+            ws[r][c + 3] = wv[i].w;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int kk = 0; kk < RK; ++kk) {
+            float xk[MT], wk[ME];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) xk[i] = xs[tt * MT + i][kk];
+#pragma unroll
+            for (int j = 0; j < ME; ++j) wk[j] = ws[ee + EW * j][kk];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < ME; ++j) acc[i][j] = fmaf(xk[i], wk[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
     // x with 8-element blocks stored in the order 0,4,1,5,2,6,3,7: the A operand
-    // layout of the decode path's int4 nibble-pair dequantization
+    // layout of the decode path's int4 nibble-pair dequantization (after the
+    // products, so that its loads find this slice of x in the cache)
     if (x_perm && blockIdx.y == 0) {
         for (int64_t idx = tid; idx < static_cast<int64_t>(TT) * (slice / 8); idx += 256) {
             const int64_t t = t0 + idx / (slice / 8);
@@ -65,42 +121,6 @@ __global__ __launch_bounds__(256) void router_partials_kernel(const uint16_t* __
         }
     }
 
-    for (int64_t k0 = kb; k0 < kb + slice; k0 += RK) {
-        for (int idx = tid; idx < TT * (RK / 4); idx += 256) {  // x: TT x 32 bf16
-            const int r = idx / (RK / 4), c = (idx % (RK / 4)) * 4;
-            const int64_t t = t0 + r;
-            uint2 v = make_uint2(0u, 0u);
-            if (t < T) v = *reinterpret_cast<const uint2*>(x + t * d + k0 + c);
-            xs[r][c + 0] = __uint_as_float(v.x << 16);
-            xs[r][c + 1] = __uint_as_float(v.x & 0xFFFF0000u);
-            xs[r][c + 2] = __uint_as_float(v.y << 16);
-            xs[r][c + 3] = __uint_as_float(v.y & 0xFFFF0000u);
-        }
-        for (int idx = tid; idx < EE * (RK / 4); idx += 256) {  // router: EE x 32 fp32
-            const int r = idx / (RK / 4), c = (idx % (RK / 4)) * 4;
-            const int64_t e = e0 + r;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (e < E) v = *reinterpret_cast<const float4*>(wr + e * d + k0 + c);
-            ws[r][c + 0] = v.x;
-            ws[r][c + 1] = v.y;
-            ws[r][c + 2] = v.z;
-            ws[r][c + 3] = v.w;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int kk = 0; kk < RK; ++kk) {
-            float xv[MT], wv[ME];
-#pragma unroll
-            for (int i = 0; i < MT; ++i) xv[i] = xs[tt * MT + i][kk];
-#pragma unroll
-            for (int j = 0; j < ME; ++j) wv[j] = ws[ee + EW * j][kk];
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int j = 0; j < ME; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
-        }
-        __syncthreads();
-    }
     float* out = partials + static_cast<int64_t>(blockIdx.z) * T * E;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -315,8 +335,12 @@ hipError_t launch_router_partials(const uint16_t* x, const float* wr, int64_t T,
     const int64_t slice = d / p.slices;
     switch (p.kind) {
         case 0:
-            MOE_LAUNCH((router_partials_kernel<16, 16, 1, 1>), grid, dim3(256), 0, stream, x,
-                               wr, T, d, E, slice, partials, x_perm);
+            if (slice % 128 == 0)
+                MOE_LAUNCH((router_partials_kernel<16, 16, 1, 1, 128>), grid, dim3(256), 0, stream, x,
+                           wr, T, d, E, slice, partials, x_perm);
+            else
+                MOE_LAUNCH((router_partials_kernel<16, 16, 1, 1>), grid, dim3(256), 0, stream, x,
+                           wr, T, d, E, slice, partials, x_perm);
             break;
         case 1:
             MOE_LAUNCH((router_partials_kernel<128, 16, 8, 1>), grid, dim3(256), 0, stream, x,
