@@ -56,7 +56,7 @@ constexpr int64_t kSplitRows = 2048;
 // Workspace sections (byte offsets from the workspace base).
 struct Layout {
     size_t partials, logits, ids, gates, counts, offsets, tile_base, perm, inv, chunks, nchunks,
-        wparts, routing_end, x_perm, H, O, O2, total;
+        routing_end, x_perm, H, O, O2, total;
     size_t xq, sxq, hq, shq, total_fp8;  // fp8 experts: quantized x and H rows, row scales
     int slices;
     int max_chunks;
@@ -91,7 +91,6 @@ Layout layout(const moe_dims& d) {
     L.inv = take(P * 4);
     L.chunks = take(static_cast<size_t>(L.max_chunks) * 16);
     L.nchunks = take(4);
-    L.wparts = take(plan.kind == 4 ? 3 * E * static_cast<size_t>(d.d) * 2 : 0);
     L.routing_end = off;
     L.x_perm = take(T * static_cast<size_t>(d.d) * 2);
     L.H = take((P + T) * static_cast<size_t>(d.h) * 2);
@@ -279,7 +278,6 @@ struct Routing {
     int32_t* inv;
     int4* chunks;
     int32_t* nchunks;
-    uint16_t* wparts;
 };
 
 Routing carve(const moe_dims& d, void* ws) {
@@ -297,7 +295,6 @@ Routing carve(const moe_dims& d, void* ws) {
     R.inv = reinterpret_cast<int32_t*>(b + L.inv);
     R.chunks = reinterpret_cast<int4*>(b + L.chunks);
     R.nchunks = reinterpret_cast<int32_t*>(b + L.nchunks);
-    R.wparts = reinterpret_cast<uint16_t*>(b + L.wparts);
     return R;
 }
 
@@ -371,7 +368,7 @@ int run_routing(const moe_dims& d, const uint16_t* x, const float* wr, const flo
                 int small_rows, int tile_rows, hipStream_t s) {
     const moe::RouterPlan plan = moe::router_plan(d.T, d.d, d.E);
     CHECK(timed(MOE_STAGE_ROUTER, s, "router launch", [&] {
-        return moe::launch_router_partials(x, wr, d.T, d.d, d.E, plan, R.partials, x_perm, R.wparts, s);
+        return moe::launch_router_partials(x, wr, d.T, d.d, d.E, plan, R.partials, x_perm, s);
     }));
     if (small_routing(d)) {
         CHECK(timed(MOE_STAGE_TOPK, s, "small routing launch", [&] {

@@ -84,10 +84,9 @@ constexpr int kMaxRouterSlices = 16;
 constexpr int64_t kRouterMfmaTokens = 256;
 // K2: partials[s][t][e] = sum over slice s of x[t, :] router_w[e, :]   (fp32)
 // (optional) x_perm: x with 8-element blocks in the order 0,4,1,5,2,6,3,7
-// wparts: [3][E][d] bf16 scratch for the split weights (MFMA plan only)
 hipError_t launch_router_partials(const uint16_t* x, const float* wr, int64_t T, int64_t d,
                                   int64_t E, const RouterPlan& plan, float* partials,
-                                  uint16_t* x_perm, uint16_t* wparts, hipStream_t stream);
+                                  uint16_t* x_perm, hipStream_t stream);
 // K2: logits = sum of slices (+ bias), top-k per token (ties to the lower id), sigmoid gates
 hipError_t launch_topk(const float* partials, int slices, const float* bias, int64_t T, int64_t E,
                        int top_k, float* logits, int32_t* ids, float* gates, int32_t* ids_copy,

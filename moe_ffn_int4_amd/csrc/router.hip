@@ -11,7 +11,7 @@
 // on bf16 MFMA without losing precision: each fp32 router weight is split
 // exactly into three bf16 parts (hi + mid + lo, every part the rounding of
 // what the previous parts leave), so each product x * part is exact and the
-// matrix cores sum x * w in fp32 (router_mfma_kernel).
+// matrix cores sum x * w in fp32 (router_gemm_kernel).
 //
 // router_partials_kernel<TT, EE, MT, ME>: a 256-thread block computes a
 // TT-token x EE-expert tile over one slice of the reduction dimension; each
@@ -137,17 +137,17 @@ __global__ __launch_bounds__(256) void router_partials_kernel(const uint16_t* __
 RouterPlan router_plan(int64_t T, int64_t d, int64_t E) {
     RouterPlan p{};
     if (T >= kRouterMfmaTokens) {
-        // bf16 MFMA on the split weights: one wave per 32 tokens x 16 or 32
-        // experts; slices of the reduction (multiples of 64 wide) until there
-        // are about 8192 waves (each wave's loads are latency-bound)
+        // bf16 MFMA on the exactly split weights: blocks of 128 tokens x up to
+        // 128 experts (ee), slices of the reduction (multiples of 32 wide)
+        // until there are about 512 blocks
         p.kind = 4;
-        p.tt = 32;
-        p.ee = E <= 16 ? 16 : 32;
-        const int64_t waves = ((T + 31) / 32) * ((E + p.ee - 1) / p.ee);
-        const int64_t want = (8192 + waves - 1) / waves;
+        p.tt = 128;
+        p.ee = E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : 128;
+        const int64_t blocks = ((T + 127) / 128) * ((E + p.ee - 1) / p.ee);
+        const int64_t want = (512 + blocks - 1) / blocks;
         int64_t s = 1;
-        for (int64_t c = 1; c <= d / 64 && c <= kMaxRouterSlices; ++c)
-            if ((d / 64) % c == 0 && c <= want) s = c;
+        for (int64_t c = 1; c <= d / 32 && c <= kMaxRouterSlices; ++c)
+            if ((d / 32) % c == 0 && c <= want) s = c;
         p.slices = static_cast<int>(s);
         return p;
     }
@@ -178,155 +178,174 @@ RouterPlan router_plan(int64_t T, int64_t d, int64_t E) {
     return p;
 }
 
-// fp32 router weights [E, d] -> three bf16 parts [3][E][d] with
-// hi + mid + lo == w exactly: hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid)
-// (each difference is exact in fp32, and what is left after mid fits 8 bits)
-__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr, int64_t n,
-                                                           uint16_t* __restrict__ parts) {
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const float w = wr[i];
-        const uint16_t hi = f32_to_bf16(w);
-        const float r1 = w - bf16_to_f32(hi);
-        const uint16_t mid = f32_to_bf16(r1);
-        const float r2 = r1 - bf16_to_f32(mid);
-        parts[i] = hi;
-        parts[n + i] = mid;
-        parts[2 * n + i] = f32_to_bf16(r2);
-    }
+// Prefill batches: router logits on the bf16 matrix cores without losing
+// the fp32 weights. Each fp32 weight w is split exactly into three bf16
+// parts, hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid) (each
+// difference is exact in fp32, and what is left after mid fits 8 bits), so
+// hi + mid + lo == w, every product x * part is exact and the matrix cores
+// sum x * w in fp32.
+//
+// router_gemm_kernel<EC>: a block is 4 waves over 128 tokens (32 per wave:
+// two 16-row v_mfma_f32_16x16x32_bf16 tiles) and EC experts (blockIdx.y: a
+// chunk of EC, EC in 16..128) for one slice of the reduction (blockIdx.z).
+// Per 32-wide step the block reads its EC x 32 fp32 weights once (8 threads
+// per expert row, one float4 each), splits them in registers and stores the
+// three parts in LDS in B-fragment order (part p, expert tile j: lane
+// (n, q) at (q * 16 + n) * 16 bytes); the waves then read them against their
+// own tokens' A fragments, which come straight from x. The next step's loads
+// are requested before this step's products. Blocks of expert chunk 0 also
+// write x_perm for their tokens and columns. Partial sums go to
+// out[slice][t][e] and are added in slice order by the top-k kernel.
+namespace {
+constexpr int kRouterStepBytes = 1024;  // one 16-expert x 32-column bf16 fragment tile
 }
 
-// One wave per 32-token x (16 JN)-expert tile over one slice of the
-// reduction: 2 x JN v_mfma_f32_16x16x32_bf16 tiles, three MFMAs per tile and
-// 32-wide step (one per weight part), with the next step's fragments loaded
-// before the current step's MFMAs. A fragments come straight from x, B
-// fragments from the split weights (rows past T or E re-read the last row;
-// not stored). Partial sums go to out[slice][t][e]. The waves also write
-// x_perm (when asked) for their slice's columns of the tile's tokens, rows
-// spread over the tile's n_et waves.
-template <int JN>
-__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ parts,
-                                                          int64_t T, int64_t d, int64_t E, int n_et,
-                                                          int64_t slice, float* __restrict__ out,
+template <int EC>
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ wr, int64_t T,
+                                                          int64_t d, int64_t E, int64_t slice,
+                                                          float* __restrict__ out,
                                                           uint16_t* __restrict__ x_perm) {
-    const int lane = threadIdx.x & 63;
-    const int64_t task = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int64_t n_tt = (T + 31) / 32;
-    if (task >= n_tt * n_et) return;
-    const int64_t tt = task / n_et;
-    const int et = static_cast<int>(task % n_et);
+    constexpr int NJ = EC / 16;                    // expert tiles
+    constexpr int PART = NJ * kRouterStepBytes;    // one bf16 part of the step
+    constexpr int WI = (EC * 8 + 255) / 256;       // float4 weight loads per thread
+    __shared__ __attribute__((aligned(16))) uint8_t bs[3 * PART];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, kq = lane >> 4;
-    const int64_t kb = static_cast<int64_t>(blockIdx.y) * slice;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 128 + 32 * w;
+    const int64_t e0 = static_cast<int64_t>(blockIdx.y) * EC;
+    const int64_t kb = static_cast<int64_t>(blockIdx.z) * slice;
+    const int steps = static_cast<int>(slice / 32);
+
+    // A: rows t0 + 16 i + l16 (past T: the last row, not stored), columns 8 kq ..
     const uint16_t* xr[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        int64_t t = tt * 32 + 16 * i + l16;
+        int64_t t = t0 + 16 * i + l16;
         t = t < T ? t : T - 1;
         xr[i] = x + t * d + kb + kq * 8;
     }
-    const uint16_t* wp[JN][3];
+    // B: thread -> expert row er[u] = tid / 8 + 32 u of the chunk, columns 4 (tid % 8) ..
+    const float* wrow[WI];
+    int boff[WI];
+    bool bval[WI];
 #pragma unroll
-    for (int j = 0; j < JN; ++j) {
-        int64_t e = static_cast<int64_t>(et) * 16 * JN + 16 * j + l16;
-        e = e < E ? e : E - 1;
-#pragma unroll
-        for (int q = 0; q < 3; ++q) wp[j][q] = parts + (q * E + e) * d + kb + kq * 8;
+    for (int u = 0; u < WI; ++u) {
+        const int r = tid / 8 + 32 * u;
+        const int c = (tid & 7) * 4;
+        bval[u] = r < EC && e0 + r < E;
+        wrow[u] = wr + (bval[u] ? (e0 + r) * d : 0) + kb + c;
+        boff[u] = (r / 16) * kRouterStepBytes + ((c / 8) * 16 + (r % 16)) * 16 + (c % 8) * 2;
     }
-    f32x4 acc[2][JN];
+
+    f32x4 acc[2][NJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < JN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 a[2], b[JN][3], na[2], nb[JN][3];
-    auto load = [&](bf16x8 (&fa)[2], bf16x8 (&fb)[JN][3], int64_t k) __attribute__((always_inline)) {
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint4 ra[2];
+    float4 rw[WI];
+    auto load = [&](int s) __attribute__((always_inline)) {
+        const int64_t k = static_cast<int64_t>(s) * 32;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(xr[i] + k);
+        for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const uint4*>(xr[i] + k);
 #pragma unroll
-        for (int j = 0; j < JN; ++j)
-#pragma unroll
-            for (int q = 0; q < 3; ++q) fb[j][q] = *reinterpret_cast<const bf16x8*>(wp[j][q] + k);
+        for (int u = 0; u < WI; ++u)
+            rw[u] = bval[u] ? *reinterpret_cast<const float4*>(wrow[u] + k) : make_float4(0.f, 0.f, 0.f, 0.f);
     };
-    auto mma = [&](const bf16x8 (&fa)[2], const bf16x8 (&fb)[JN][3]) __attribute__((always_inline)) {
+    load(0);
+    for (int s = 0; s < steps; ++s) {
+        // split this step's weights into the three parts, in fragment order
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int u = 0; u < WI; ++u) {
+            if (tid / 8 + 32 * u >= EC) continue;
+            const float v[4] = {rw[u].x, rw[u].y, rw[u].z, rw[u].w};
+            uint16_t hi[4], mid[4], lo[4];
 #pragma unroll
-            for (int j = 0; j < JN; ++j)
-#pragma unroll
-                for (int q = 0; q < 3; ++q)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j][q], acc[i][j], 0, 0, 0);
-    };
-    // slice is a multiple of 64: steps come in pairs
-    load(a, b, 0);
-    for (int64_t k = 0; k < slice; k += 64) {
-        load(na, nb, k + 32);
-        mma(a, b);
-        load(a, b, k + 64 < slice ? k + 64 : k);  // past the end: a harmless re-read
-        mma(na, nb);
-    }
-    float* o = out + static_cast<int64_t>(blockIdx.y) * T * E;
-    // D[token][expert]: token row 4 kq + r of the 16 x 16 tile, expert column l16
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < JN; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t t = tt * 32 + 16 * i + 4 * kq + r;
-                const int64_t e = static_cast<int64_t>(et) * 16 * JN + 16 * j + l16;
-                if (t < T && e < E) o[t * E + e] = acc[i][j][r];
+            for (int e = 0; e < 4; ++e) {
+                hi[e] = f32_to_bf16(v[e]);
+                const float r1 = v[e] - bf16_to_f32(hi[e]);
+                mid[e] = f32_to_bf16(r1);
+                lo[e] = f32_to_bf16(r1 - bf16_to_f32(mid[e]));
             }
-    if (x_perm) {
-        // this slice's columns of the tile's rows r = et, et + n_et, ...;
-        // (row, 8-column piece) pairs in lane order, four in flight per lane
-        const int nr = (32 - et + n_et - 1) / n_et;
-        const int64_t per_row = slice / 8;
-        const int64_t items = static_cast<int64_t>(nr) * per_row;
-        for (int64_t base = 0; base < items; base += 256) {
-            uint4 v[4];
-            int64_t at[4];
+            *reinterpret_cast<uint2*>(bs + boff[u]) =
+                make_uint2(hi[0] | (static_cast<uint32_t>(hi[1]) << 16), hi[2] | (static_cast<uint32_t>(hi[3]) << 16));
+            *reinterpret_cast<uint2*>(bs + PART + boff[u]) =
+                make_uint2(mid[0] | (static_cast<uint32_t>(mid[1]) << 16), mid[2] | (static_cast<uint32_t>(mid[3]) << 16));
+            *reinterpret_cast<uint2*>(bs + 2 * PART + boff[u]) =
+                make_uint2(lo[0] | (static_cast<uint32_t>(lo[1]) << 16), lo[2] | (static_cast<uint32_t>(lo[3]) << 16));
+        }
+        const bf16x8 a0 = __builtin_bit_cast(bf16x8, ra[0]);
+        const bf16x8 a1 = __builtin_bit_cast(bf16x8, ra[1]);
+        if (x_perm && blockIdx.y == 0) {
+            // this lane's 8 columns of both rows, 8-element blocks in the order 0,4,1,5,2,6,3,7
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t it = base + u * 64 + lane;
-                const int64_t r = it / per_row;
-                const int64_t t = tt * 32 + et + r * n_et;
-                at[u] = (it < items && t < T) ? t * d + kb + (it - r * per_row) * 8 : -1;
-                v[u] = at[u] >= 0 ? *reinterpret_cast<const uint4*>(x + at[u]) : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (at[u] < 0) continue;
-                uint4 w;
-                w.x = (v[u].x & 0xFFFFu) | (v[u].z << 16);
-                w.y = (v[u].x >> 16) | (v[u].z & 0xFFFF0000u);
-                w.z = (v[u].y & 0xFFFFu) | (v[u].w << 16);
-                w.w = (v[u].y >> 16) | (v[u].w & 0xFFFF0000u);
-                *reinterpret_cast<uint4*>(x_perm + at[u]) = w;
+            for (int i = 0; i < 2; ++i) {
+                const int64_t t = t0 + 16 * i + l16;
+                if (t >= T) continue;
+                const uint4 v = ra[i];
+                uint4 r;
+                r.x = (v.x & 0xFFFFu) | (v.z << 16);
+                r.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+                r.z = (v.y & 0xFFFFu) | (v.w << 16);
+                r.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+                *reinterpret_cast<uint4*>(x_perm + t * d + kb + static_cast<int64_t>(s) * 32 + kq * 8) = r;
             }
         }
+        __syncthreads();
+        if (s + 1 < steps) load(s + 1);  // the next step's loads fly under the products
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+                const bf16x8 b = *reinterpret_cast<const bf16x8*>(
+                    bs + p * PART + j * kRouterStepBytes + (kq * 16 + l16) * 16);
+                acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][j], 0, 0, 0);
+                acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][j], 0, 0, 0);
+            }
+        }
+        __syncthreads();
     }
+    float* o = out + static_cast<int64_t>(blockIdx.z) * T * E;
+    // D[token][expert]: token row 4 kq + r of a 16 x 16 tile, expert column l16
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t t = t0 + 16 * i + 4 * kq + r;
+                const int64_t e = e0 + 16 * j + l16;
+                if (t < T && e < E) o[t * E + e] = acc[i][j][r];
+            }
 }
 
 hipError_t launch_router_partials(const uint16_t* x, const float* wr, int64_t T, int64_t d,
                                   int64_t E, const RouterPlan& p, float* partials,
-                                  uint16_t* x_perm, uint16_t* wparts, hipStream_t stream) {
+                                  uint16_t* x_perm, hipStream_t stream) {
     if (p.kind == 4) {
-        const int64_t n = E * d;
-        const int64_t want = (n + 255) / 256;
-        MOE_LAUNCH(router_split_kernel, dim3(static_cast<unsigned>(want < 4096 ? want : 4096)),
-                           dim3(256), 0, stream, wr, n, wparts);
         const int64_t slice = d / p.slices;
-        if (E <= 16) {
-            const int64_t tasks = (T + 31) / 32;
-            MOE_LAUNCH((router_mfma_kernel<1>),
-                               dim3(static_cast<unsigned>((tasks + 3) / 4), static_cast<unsigned>(p.slices)),
-                               dim3(256), 0, stream, x, wparts, T, d, E, 1, slice, partials, x_perm);
-        } else {
-            const int n_et = static_cast<int>((E + 31) / 32);
-            const int64_t tasks = ((T + 31) / 32) * n_et;
-            MOE_LAUNCH((router_mfma_kernel<2>),
-                               dim3(static_cast<unsigned>((tasks + 3) / 4), static_cast<unsigned>(p.slices)),
-                               dim3(256), 0, stream, x, wparts, T, d, E, n_et, slice, partials, x_perm);
+        const int ec = p.ee;
+        dim3 grid(static_cast<unsigned>((T + 127) / 128), static_cast<unsigned>((E + ec - 1) / ec),
+                  static_cast<unsigned>(p.slices));
+        switch (ec) {
+            case 16:
+                MOE_LAUNCH((router_gemm_kernel<16>), grid, dim3(256), 0, stream, x, wr, T, d, E, slice,
+                           partials, x_perm);
+                break;
+            case 32:
+                MOE_LAUNCH((router_gemm_kernel<32>), grid, dim3(256), 0, stream, x, wr, T, d, E, slice,
+                           partials, x_perm);
+                break;
+            case 64:
+                MOE_LAUNCH((router_gemm_kernel<64>), grid, dim3(256), 0, stream, x, wr, T, d, E, slice,
+                           partials, x_perm);
+                break;
+            default:
+                MOE_LAUNCH((router_gemm_kernel<128>), grid, dim3(256), 0, stream, x, wr, T, d, E, slice,
+                           partials, x_perm);
+                break;
         }
         return hipGetLastError();
     }
