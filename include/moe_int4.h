@@ -318,7 +318,8 @@ int moe_route(const moe_dims *dims, const uint16_t *x, const float *router_w,
 
 /*
  * Per-stage timing for benchmarks (not part of the layer's arithmetic).
- * While enabled, each stage of every moe_forward / moe_route call is timed by
+ * While enabled, each stage of every moe_forward / moe_route call (and each
+ * int4 quantizer call, as MOE_STAGE_QUANTIZE) is timed by
  * a pair of hipEvents that its kernels record themselves (hipExtLaunchKernel):
  * at the start of the stage's first kernel and the end of its last, so the
  * time excludes the dispatch gap before the stage. moe_profile_read waits for
@@ -338,7 +339,8 @@ enum moe_stage {
     MOE_STAGE_DECODE_UP = 6,   /* decode path: streaming up-projection */
     MOE_STAGE_DECODE_DOWN = 7, /* decode path: streaming down-projection */
     MOE_STAGE_ACT_QUANT = 8,   /* fp8 experts: per-row fp8 quantization of x and H */
-    MOE_STAGE_COUNT = 9
+    MOE_STAGE_QUANTIZE = 9,    /* K1: moe_quantize_int4 / moe_quantize_int4_tiled calls */
+    MOE_STAGE_COUNT = 10
 };
 
 /*

@@ -597,7 +597,7 @@ def unpack_int4(q: torch.Tensor) -> torch.Tensor:
 
 # ------------------------------------------------------------------ timing
 
-STAGE_COUNT = 9
+STAGE_COUNT = 10
 
 
 def hbm_read(buf: torch.Tensor, sink: torch.Tensor) -> None:

@@ -427,10 +427,10 @@ static int quantize(const float* w, int64_t rows, int64_t K, int32_t group_size,
     CHECK(check_ptr(q, "q"));
     CHECK(check_ptr(scales, "scales", 4));
     CHECK(device_ok());
-    HIP_CHECK(moe::launch_quantize_int4(w, rows, K, group_size, q, scales, tiled,
-                                        static_cast<hipStream_t>(stream)),
-              "quantize launch");
-    return MOE_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return timed(MOE_STAGE_QUANTIZE, s, "quantize launch", [&] {
+        return moe::launch_quantize_int4(w, rows, K, group_size, q, scales, tiled, s);
+    });
 }
 
 int moe_quantize_int4(const float* w, int64_t rows, int64_t K, int32_t group_size, uint8_t* q,
@@ -989,7 +989,7 @@ int moe_profile_read(double* ms, int64_t* launches, int n) {
 const char* moe_stage_name(int stage) {
     static const char* names[MOE_STAGE_COUNT] = {"router", "topk", "dispatch", "grouped_up",
                                                  "grouped_down", "combine", "decode_up", "decode_down",
-                                                 "act_quant"};
+                                                 "act_quant", "quantize"};
     return (stage >= 0 && stage < MOE_STAGE_COUNT) ? names[stage] : "unknown";
 }
 

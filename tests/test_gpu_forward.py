@@ -100,6 +100,34 @@ def test_decode_chunks_past_lds_rows(name, group):
     _check(layer, y, ids, np.arange(cfg.T))
 
 
+# Decode layers whose down projection splits its reduction over two blocks
+# (int4 groups of 128, P < 4 E, so the chunks are not sliced): an odd group
+# count (5: halves of 2 and 3 groups), 3 groups (a half of one group, so some
+# waves of the shared expert's bf16 blocks get none), and an expert chunk of
+# more rows than fit in LDS at h = 4096 (5 rows), which takes the global-A
+# branch with the split.
+ZSPLIT = {
+    "h=640, 5 groups": W.config(0).with_(T=20, E=8, h=640, top_k=1),
+    "h=384, 3 groups": W.config(0).with_(T=10, E=6, h=384, top_k=2),
+    "global-A chunk, h=4096": W.config(0).with_(T=24, E=8, h=4096, top_k=1, bias="zipf",
+                                                bias_param=3.0),
+}
+
+
+@pytest.mark.parametrize("name", list(ZSPLIT))
+def test_decode_split_reduction_cases(name):
+    cfg = ZSPLIT[name]
+    P = cfg.T * cfg.top_k
+    assert P < 4 * cfg.E and P + cfg.T <= 2048 and cfg.h >= 256  # the split's conditions
+    say(f"forward[decode]: {name} T={cfg.T} E={cfg.E} h={cfg.h} k={cfg.top_k}")
+    layer = build_layer(cfg)
+    y, ids, _ = _run(layer, "decode")
+    if "global-A" in name:
+        lds_rows = (48 * 1024) // ((cfg.h + 8) * 2)
+        assert np.bincount(ids.ravel(), minlength=cfg.E).max() > lds_rows
+    _check(layer, y, ids, np.arange(cfg.T))
+
+
 def test_tiny_layer_all_paths_agree():
     layer = build_layer(W.config(0))
     y1, i1, _ = _run(layer, "prefill")
