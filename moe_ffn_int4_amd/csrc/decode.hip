@@ -54,6 +54,7 @@ namespace moe {
 
 namespace {
 constexpr int NT = 256;
+constexpr int kStagePieces = 4;  // A pieces per thread requested together when staging
 constexpr uint32_t kMagic = 0x43004300u;   // bf16 128.0 in both halves
 constexpr uint32_t kNeg136 = 0xC308C308u;  // bf16 -136.0 in both halves
 }  // namespace
@@ -458,13 +459,32 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         WeightSlot<S> sl[U];
 #pragma unroll
         for (int p = 0; p < D; ++p) load_weights<UP, S>(sl[p], q0, q1, s0, s1, min(p, ngl > 0 ? ngl - 1 : 0));
+        // Only this block's columns (its groups glo .. ghi - 1 of the z split)
+        // are staged, at their own positions; each thread requests
+        // kStagePieces 16-byte pieces before storing any, so the staging takes
+        // one or two memory round trips instead of one per piece.
         const int64_t pitch = K + 8;  // 16-byte pad between rows
-        for (int64_t idx = tid; idx < static_cast<int64_t>(nrows) * (K / 8); idx += NT) {
-            const int r = static_cast<int>(idx / (K / 8));
-            const int64_t col = (idx - r * (K / 8)) * 8;
-            const int64_t srow = UP ? a.perm[row0 + r] / a.top_k : row0 + r;
-            *reinterpret_cast<uint4*>(a_lds + r * pitch + col) =
-                *reinterpret_cast<const uint4*>(a.a_perm + srow * K + col);
+        const int per_row = ngl * (kGroup / 8);
+        const int pieces = nrows * per_row;  // at most 16 rows of K / 8 pieces
+        for (int i0 = tid; i0 < pieces; i0 += kStagePieces * NT) {
+            uint4 v[kStagePieces];
+#pragma unroll
+            for (int u = 0; u < kStagePieces; ++u) {
+                // pieces past the end re-read the last one (not stored)
+                const int idx = min(i0 + u * NT, pieces - 1);
+                const int r = idx / per_row;
+                const int col = glo * kGroup + (idx - r * per_row) * 8;
+                const int64_t srow = UP ? a.perm[row0 + r] / a.top_k : row0 + r;
+                v[u] = *reinterpret_cast<const uint4*>(a.a_perm + srow * K + col);
+            }
+#pragma unroll
+            for (int u = 0; u < kStagePieces; ++u) {
+                const int idx = i0 + u * NT;
+                if (idx >= pieces) break;
+                const int r = idx / per_row;
+                const int col = glo * kGroup + (idx - r * per_row) * 8;
+                *reinterpret_cast<uint4*>(a_lds + r * pitch + col) = v[u];
+            }
         }
         __syncthreads();
         const uint16_t* lrow = a_lds + m * pitch + (S == 1 ? kq * 32 : kq * 8) + glo * kGroup;
