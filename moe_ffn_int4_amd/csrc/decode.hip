@@ -716,11 +716,13 @@ static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, int shar
 // memory, DS bf16 chunks, DL routed chunks with A staged in LDS; smaller
 // int4 groups hold more scales per slot and take shallower rings (measured on
 // the Scout decode layer: groups of 64 up 119 -> 108 us, groups of 32 up
-// 126 -> 118 us and down 86 -> 79 us against the depths of groups of 128)
+// 126 -> 118 us and down 86 -> 79 us against the depths of groups of 128).
+// Groups of 64, up: DR 3 needs 154 VGPRs, two waves per SIMD; DR 2 fits in
+// 128, three waves: 104.8 -> 98.2 us.
 hipError_t launch_decode_up(const DecodeArgs& args, int max_chunks, int shared_chunks,
                             hipStream_t stream) {
     if (args.wf0) return launch_decode<true, 3, 1, 7, true, 1>(args, max_chunks, shared_chunks, stream);
-    if (args.spt == 2) return launch_decode<true, 3, 1, 5, false, 2>(args, max_chunks, shared_chunks, stream);
+    if (args.spt == 2) return launch_decode<true, 2, 1, 5, false, 2>(args, max_chunks, shared_chunks, stream);
     if (args.spt == 4) return launch_decode<true, 2, 1, 4, false, 4>(args, max_chunks, shared_chunks, stream);
     if (args.sliced) return launch_decode<true, 3, 1, 5, false, 1, true>(args, max_chunks, shared_chunks, stream);
     return launch_decode<true, 3, 1, 5, false, 1>(args, max_chunks, shared_chunks, stream);
