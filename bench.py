@@ -440,11 +440,13 @@ def measure(ci: int, args, steps: int, warmup: int, cpu_sample: int, cpu_seconds
 
     def roofline(stage):
         """algorithmic bytes (decode) or FLOPs (prefill) of one launch of
-        `stage`, averaged over the timed steps, over its mean launch time"""
+        `stage`, averaged over its launches in the timed steps (the decode
+        projections launch twice a step: the shared expert's chunks and the
+        routed ones), over its mean launch time"""
         st_ms, st_n = launched[stage]
         per_step = [u.get(stage, (0, 0.0)) for u in units]
-        byts = sum(per_step[i % nlayers][0] for i in range(steps)) / steps
-        flops = sum(per_step[i % nlayers][1] for i in range(steps)) / steps
+        byts = sum(per_step[i % nlayers][0] for i in range(steps)) / st_n
+        flops = sum(per_step[i % nlayers][1] for i in range(steps)) / st_n
         mean_s = st_ms / st_n / 1e3
         if decode_like:
             achieved = byts / mean_s / 1e9
@@ -453,7 +455,7 @@ def measure(ci: int, args, steps: int, warmup: int, cpu_sample: int, cpu_seconds
         else:
             achieved = flops / mean_s / 1e12
             # the launch's FLOPs at their own dtype's peak: fp8 routed rows, bf16 the rest
-            f8 = sum(units[i % nlayers]["fp8_flops"].get(stage, 0.0) for i in range(steps)) / steps
+            f8 = sum(units[i % nlayers]["fp8_flops"].get(stage, 0.0) for i in range(steps)) / st_n
             peak = flops / ((flops - f8) / BF16_MFMA_PEAK_TFLOPS + f8 / FP8_MFMA_PEAK_TFLOPS)
             roof = {"bound": "mfma", "achieved": achieved, "peak": peak,
                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None}
@@ -463,6 +465,7 @@ def measure(ci: int, args, steps: int, warmup: int, cpu_sample: int, cpu_seconds
             roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
         roof["kernel"] = stage
         roof["mean_launch_us"] = mean_s * 1e6
+        roof["launches_per_step"] = st_n / steps
         roof["algorithmic_per_launch"] = byts if decode_like else flops
         return roof
 
