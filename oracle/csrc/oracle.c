@@ -268,8 +268,11 @@ static uint8_t fp8_bits(double v)
     return (uint8_t)(sign | (uint8_t)(((ex - 1 + 7) << 3) | mant));
 }
 
+/* value of an E4M3 bit pattern; exponent and mantissa fields all ones (0x7F,
+ * 0xFF) encode NaN, the format having no infinities */
 double oracle_fp8_value(uint8_t c)
 {
+    if ((c & 0x7F) == 0x7F) return NAN;
     int ef = (c >> 3) & 15, m = c & 7;
     double v = ef == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, ef - 7);
     return (c & 0x80) ? -v : v;
