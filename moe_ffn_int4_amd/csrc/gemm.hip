@@ -64,10 +64,8 @@ static_assert(BM == 128, "tile table row height");
 //
 // LDS holds 2 stages of one 32-wide reduction step: 8 A sub-tiles then
 // 16 B sub-tiles, each 16 rows x 32 k = 1 KB in MFMA fragment order: the
-// 16-byte piece (row n, k 8q..8q+7) sits at slot 16 q + (n ^ c[q]), c = {0, 4,
-// 10, 14}. A fragment read (lane -> n = lane % 16, q = lane / 16) and a staging
-// write (lane -> n = lane / 4, q = lane % 4) then touch distinct banks in every
-// group of 8 or 16 lanes.
+// 16-byte piece (row n, k 8q..8q+7) sits at slot 16 q + (n ^ 2q) (frag_slot),
+// where fragment reads and staging writes are free of bank conflicts.
 //
 // Step k: the global loads of step k+2 are issued first, into the register
 // set that step k+1's data is not in; each wave then reads all 12 of its
@@ -78,9 +76,13 @@ static_assert(BM == 128, "tile table row height");
 // Loads are not issued under branches: a load under a branch is waited on
 // where the branch joins, which would serialize it with the MFMAs.
 
-template <bool UP, bool ROUTED>
+// MI: A sub-tiles (16 rows) per wave: 4 for a full 128-row tile, 2 for a
+// routed int4 tile of at most 64 rows (an expert's tail), which then issues
+// half the MFMAs and stages half the A rows, with the same B staging.
+template <bool UP, bool ROUTED, int MI = 4>
 __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& tile, int nt,
                                           uint8_t* lds) {
+    static_assert(MI == 4 || MI == 2, "full or half tile");
     // ROUTED: int4 B (routed experts); otherwise bf16 B: the shared expert, or
     // routed experts held in bf16 (wb0 / wb1)
     const bool routed_rows = tile.group < a.E;
@@ -96,7 +98,7 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
     const int steps = static_cast<int>(K / BK);
 
     // ---- A staging: thread -> rows (tid/4) + 64 i, piece q = tid % 4
-    constexpr int AP = BM * BK / 8 / NT;  // 2 pieces per thread
+    constexpr int AP = MI / 2;  // 2 pieces per thread (128 rows), 1 for a half tile
     const uint16_t* arow[AP];
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
@@ -184,13 +186,13 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         }
     };
 
-    f32x4 acc[4][8];
+    f32x4 acc[MI][8];
 
     // fragment read offsets: lane's slot, this wave's A and B sub-tiles
     const int lslot = frag_slot(lane & 15, lane >> 4);
-    int a_off[4], b_off[8];
+    int a_off[MI], b_off[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a_off[i] = (wm * 4 + i) * SUB + lslot;
+    for (int i = 0; i < MI; ++i) a_off[i] = (wm * MI + i) * SUB + lslot;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         b_off[j] = ASUB * SUB + lslot +
@@ -202,20 +204,20 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
     auto mfma_step = [&](int stage, auto first) __attribute__((always_inline)) {
         constexpr bool FIRST = decltype(first)::value;
         const uint8_t* st = lds + stage * STAGE_BYTES;
-        bf16x8 fa[4], fb[8];
+        bf16x8 fa[MI], fb[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(st + b_off[j]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i]);
+        for (int i = 0; i < MI; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     fa[i], fb[j], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i][j], 0, 0, 0);
-        // scheduling groups: the 12 LDS reads, then the 32 MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+        // scheduling groups: the 8 + MI LDS reads, then the 8 MI MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 8 + MI, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8 * MI, 0);
     };
 
     // step k computes from LDS stage k & 1; its loop iteration first requests
@@ -251,10 +253,10 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
     // ---- epilogue: D[row][col], row = 4 * lq + r inside a 16 x 16 sub-tile, col = l16
     const int l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = wm * 64 + i * 16 + lq * 4 + r;
+            const int row = wm * 16 * MI + i * 16 + lq * 4 + r;
             if (row >= tile.nrows) continue;
             const int64_t orow = tile.row0 + row;
             if (UP) {
@@ -443,6 +445,7 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(GroupedGemmArgs a) 
     Tile tile;
     if (!find_tile<BM>(a, mt, tile)) return;
     if (tile.group < a.E && a.wf0) gemm_tile_fp8<UP>(a, tile, nt, lds);
+    else if (tile.group < a.E && !a.wb0 && tile.nrows <= BM / 2) gemm_tile<UP, true, 2>(a, tile, nt, lds);
     else if (tile.group < a.E && !a.wb0) gemm_tile<UP, true>(a, tile, nt, lds);
     else gemm_tile<UP, false>(a, tile, nt, lds);
 }
