@@ -14,11 +14,18 @@ in the 256 MB last-level cache from the step before.
 
 Prints ONE JSON line: the driver's fields plus
   roofline      the dominant kernel: algorithmic bytes (or FLOPs) per launch
-                divided by its mean launch time, timed with HIP events recorded
-                by the library around each launch on the caller's stream;
+                divided by its mean launch time, from HIP events the kernels
+                record at their own start and end (a second, eager pass over
+                the same steps), with the rocprofv3 counter traffic when the
+                recorded measurement matches the kernel's sources;
   cpu_baseline  the CPU oracle (per-token C loop, fp64) timed on the host's
-                cores over a bounded sample of the same workload;
-  detail        per-stage times and whole-step rates.
+                cores over a bounded sample of the same workload, in tokens/s
+                and GFLOP/s;
+  detail        per-stage times, whole-step rates (HBM GB/s of every stage's
+                algorithmic bytes, layer TFLOP/s, the grouped GEMMs' TFLOP/s),
+                the practical HBM ceiling and the quantizer leg;
+  prefill       with the default decode layer, the three prefill layers timed
+                in the same run, each with its own roofline and CPU sample.
 """
 from __future__ import annotations
 
@@ -289,7 +296,10 @@ def cpu_baseline(layer, n_sample, dev, min_seconds=10.0):
     if omp.isdigit():
         cores = min(cores, int(omp))
     return ref, rows, {
-        "value": n * reps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "value": n * reps / dt, "unit": "tokens/s",
+        # the layer's algorithmic FLOPs per token times the tokens run
+        "GFLOP_per_s": n * reps * (cfg.flops() / cfg.T) / dt / 1e9,
+        "cores": cores, "kind": "oracle",
         "cpu_model": cpu_model(), "omp_num_threads": omp or None,
         "sample": f"{n} of the {cfg.T} tokens of the first layer copy (fp64 per-token C loop, "
                   f"{len(set(ids.ravel().tolist()))} experts), run {reps} times; {dt:.2f} s wall",
@@ -480,6 +490,14 @@ def measure(ci: int, args, steps: int, warmup: int, cpu_sample: int, cpu_seconds
         roof["practical_hbm"] = dict(ceiling, frac_of_read=roof["achieved"] / ceiling["read_GBps"])
 
     step_bytes = sum(units[i % nlayers]["step_bytes"] for i in range(steps)) / steps
+    # the grouped GEMM kernels alone (routed and shared up and down projections
+    # on MFMA tiles): their FLOPs over their summed kernel time
+    gemm_stages = [k for k in ("grouped_up", "grouped_down") if k in launched]
+    gemm_tflops = None
+    if gemm_stages:
+        gf = sum(units[i % nlayers].get(k, (0, 0.0))[1] for k in gemm_stages for i in range(steps))
+        gt = sum(launched[k][0] for k in gemm_stages) / 1e3
+        gemm_tflops = gf / gt / 1e12
     detail = {
         "stages_us_per_step": {k: round(v[0] * 1e3 / steps, 2) for k, v in launched.items()},
         # the whole layer: algorithmic bytes of every stage's weights and
@@ -487,6 +505,7 @@ def measure(ci: int, args, steps: int, warmup: int, cpu_sample: int, cpu_seconds
         "step_hbm_GBps": step_bytes / (wall / steps) / 1e9,
         "step_hbm_frac": step_bytes / (wall / steps) / 1e9 / HBM_PEAK_GBPS,
         "step_TFLOPs": cfg0.flops() / (wall / steps) / 1e12,
+        "gemm_TFLOPs": gemm_tflops,
         "touched_experts": [u["touched"] for u in units],
         "layer_copies": nlayers,
         "path": args.path,
@@ -597,6 +616,7 @@ def main() -> int:
                 "steps": r["steps"], "warmup": r["warmup"],
                 "ms_per_step": r["ms_per_step"], "tokens_per_s": r["value"],
                 "layer_TFLOPs": r["detail"]["step_TFLOPs"],
+                "gemm_TFLOPs": r["detail"]["gemm_TFLOPs"],
                 "roofline": r["roofline"],
                 "stages_us_per_step": r["detail"]["stages_us_per_step"],
                 "touched_experts": r["detail"]["touched_experts"],
