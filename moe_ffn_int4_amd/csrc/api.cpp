@@ -805,9 +805,22 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
                 CHECK(stream_down(hch, hsplit, side->stream));
             }
         }
-        CHECK(timed(MOE_STAGE_UP, s, "grouped up launch", [&] {
-            return wide ? moe::launch_grouped_up256(g, s) : moe::launch_grouped_up(g, s);
-        }));
+        // hybrid: the large routed experts on 128-row tiles, then the shared
+        // expert alone on 256-row tiles (a plain bf16 GEMM over every token,
+        // which the 256-row kernel runs faster)
+        auto grouped = [&](bool up) {
+            if (!hybrid) {
+                g.tile_mode = moe::kTilesAll;
+                return wide ? (up ? moe::launch_grouped_up256(g, s) : moe::launch_grouped_down256(g, s))
+                            : (up ? moe::launch_grouped_up(g, s) : moe::launch_grouped_down(g, s));
+            }
+            g.tile_mode = moe::kTilesRouted;
+            hipError_t e = up ? moe::launch_grouped_up(g, s) : moe::launch_grouped_down(g, s);
+            if (e != hipSuccess) return e;
+            g.tile_mode = moe::kTilesShared;
+            return up ? moe::launch_grouped_up256(g, s) : moe::launch_grouped_down256(g, s);
+        };
+        CHECK(timed(MOE_STAGE_UP, s, "grouped up launch", [&] { return grouped(true); }));
         if (ex8) {
             if (hybrid) HIP_CHECK(hipStreamWaitEvent(s, side->mid, 0), "hipStreamWaitEvent");
             CHECK(quantize_h());
@@ -837,9 +850,7 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
         g.sh1 = nullptr;
         g.h_out = nullptr;
         g.o_out = O;
-        CHECK(timed(MOE_STAGE_DOWN, s, "grouped down launch", [&] {
-            return wide ? moe::launch_grouped_down256(g, s) : moe::launch_grouped_down(g, s);
-        }));
+        CHECK(timed(MOE_STAGE_DOWN, s, "grouped down launch", [&] { return grouped(false); }));
         if (hybrid) {
             HIP_CHECK(hipEventRecord(side->join, side->stream), "hipEventRecord");
             HIP_CHECK(hipStreamWaitEvent(s, side->join, 0), "hipStreamWaitEvent");

@@ -430,7 +430,8 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(GroupedGemmArgs a) 
 
     // ---- block -> (row tile, column tile), XCD-aware (see the file comment)
     const int ncol = static_cast<int>(UP ? a.N / (BN / 2) : (a.N + BN - 1) / BN);
-    const int nrow = a.tile_base[a.E + 1];
+    // kTilesRouted: the routed tiles only (they lead the table)
+    const int nrow = a.tile_base[a.tile_mode == kTilesRouted ? a.E : a.E + 1];
     constexpr int kGroupRows = 8;
     int lin;
     if (!xcd_tile(blockIdx.x, static_cast<int64_t>(a.tile_base[a.E]) * ncol, static_cast<int64_t>(nrow) * ncol,
@@ -453,7 +454,8 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(GroupedGemmArgs a) 
 static unsigned max_row_tiles(const GroupedGemmArgs& a) {
     // each routed expert adds at most one partial tile beyond P / BM
     const int64_t e_bound = a.E < a.P ? a.E : a.P;
-    return static_cast<unsigned>((a.P + BM - 1) / BM + e_bound + (a.T + BM - 1) / BM);
+    const int64_t shared = a.tile_mode == kTilesRouted ? 0 : (a.T + BM - 1) / BM;
+    return static_cast<unsigned>((a.P + BM - 1) / BM + e_bound + shared);
 }
 
 static constexpr size_t kGemmLds = 2 * 24 * 1024;  // 2 stages of 8 A + 16 B sub-tiles

@@ -472,11 +472,13 @@ template <bool UP, bool F8>
 __global__ __launch_bounds__(NT2, 1) void grouped_gemm256_kernel(GroupedGemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int ncol = UP ? static_cast<int>(a.N / (BN2 / 2)) : static_cast<int>((a.N + BN2 - 1) / BN2);
-    const int nrow = a.tile_base[a.E + 1];
+    // kTilesShared: the shared expert alone, 256-row tiles of its T rows
+    const bool shared_only = a.tile_mode == kTilesShared;
+    const int nrow = shared_only ? static_cast<int>((a.T + BM2 - 1) / BM2) : a.tile_base[a.E + 1];
+    const int64_t routed = shared_only ? 0 : static_cast<int64_t>(a.tile_base[a.E]) * ncol;
     constexpr int kGroupRows = 4;
     int lin;
-    if (!xcd_tile(blockIdx.x, static_cast<int64_t>(a.tile_base[a.E]) * ncol, static_cast<int64_t>(nrow) * ncol,
-                  tile_weight(a), lin))
+    if (!xcd_tile(blockIdx.x, routed, static_cast<int64_t>(nrow) * ncol, tile_weight(a), lin))
         return;
     const int span = kGroupRows * ncol;
     const int first_row = (lin / span) * kGroupRows;
@@ -485,7 +487,14 @@ __global__ __launch_bounds__(NT2, 1) void grouped_gemm256_kernel(GroupedGemmArgs
     const int nt = (lin % span) / rows_here;
 
     Tile tile;
-    if (!find_tile<BM2>(a, mt, tile)) return;
+    if (shared_only) {
+        tile.group = a.E;
+        tile.row0 = a.P + static_cast<int64_t>(mt) * BM2;
+        const int64_t left = a.T - static_cast<int64_t>(mt) * BM2;
+        tile.nrows = static_cast<int>(left < BM2 ? left : BM2);
+    } else if (!find_tile<BM2>(a, mt, tile)) {
+        return;
+    }
     if (F8 && tile.group < a.E) gemm256_tile_fp8<UP>(a, tile, nt, lds);
     else if (!F8 && tile.group < a.E && !a.wb0 && tile.nrows <= 128) gemm256_tile<UP, true, 4>(a, tile, nt, lds);
     else if (!F8 && tile.group < a.E && !a.wb0) gemm256_tile<UP, true>(a, tile, nt, lds);
@@ -493,6 +502,7 @@ __global__ __launch_bounds__(NT2, 1) void grouped_gemm256_kernel(GroupedGemmArgs
 }
 
 static unsigned max_row_tiles256(const GroupedGemmArgs& a) {
+    if (a.tile_mode == kTilesShared) return static_cast<unsigned>((a.T + BM2 - 1) / BM2);
     const int64_t e_bound = a.E < a.P ? a.E : a.P;
     return static_cast<unsigned>((a.P + BM2 - 1) / BM2 + e_bound + (a.T + BM2 - 1) / BM2);
 }
@@ -513,14 +523,18 @@ static hipError_t launch256(const GroupedGemmArgs& a, unsigned ncol, hipStream_t
     return hipGetLastError();
 }
 
+// the shared expert's tiles are bf16 whatever the routed experts are: a
+// shared-only launch takes the bf16 / int4 instantiation
 hipError_t launch_grouped_up256(const GroupedGemmArgs& a, hipStream_t stream) {
     const unsigned ncol = static_cast<unsigned>(a.N / (BN2 / 2));
-    return a.wf0 ? launch256<true, true>(a, ncol, stream) : launch256<true, false>(a, ncol, stream);
+    return a.wf0 && a.tile_mode != kTilesShared ? launch256<true, true>(a, ncol, stream)
+                                                : launch256<true, false>(a, ncol, stream);
 }
 
 hipError_t launch_grouped_down256(const GroupedGemmArgs& a, hipStream_t stream) {
     const unsigned ncol = static_cast<unsigned>((a.N + BN2 - 1) / BN2);
-    return a.wf0 ? launch256<false, true>(a, ncol, stream) : launch256<false, false>(a, ncol, stream);
+    return a.wf0 && a.tile_mode != kTilesShared ? launch256<false, true>(a, ncol, stream)
+                                                : launch256<false, false>(a, ncol, stream);
 }
 
 }  // namespace moe

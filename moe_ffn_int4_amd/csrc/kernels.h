@@ -135,14 +135,22 @@ struct GroupedGemmArgs {
     uint16_t* h_out;         // up: H [P + T, h] bf16
     float* o_out;            // down: O [P + T, d] fp32
     int routed_weight;       // time of a routed tile in eighths of a shared one (xcd_tile)
+    int tile_mode;           // kTilesAll, kTilesRouted or kTilesShared
 };
+
+// Which row tiles a grouped GEMM launch takes: every tile of the table; the
+// table's routed tiles only; or the shared expert alone, in tiles of the
+// launch's own height built from T (the table is not read).
+constexpr int kTilesAll = 0;
+constexpr int kTilesRouted = 1;
+constexpr int kTilesShared = 2;
 
 // K4 (routed) + K6a (shared): H = silu(A W1^T) * (A W3^T), one launch
 hipError_t launch_grouped_up(const GroupedGemmArgs& args, hipStream_t stream);
 // K5 (routed) + K6b (shared): O = H W2^T, one launch
 hipError_t launch_grouped_down(const GroupedGemmArgs& args, hipStream_t stream);
 // the same two launches with 256 x 256 tiles (tile table of kPrefillBM2 rows;
-// int4 or bf16 routed experts, not fp8)
+// int4, bf16 or fp8 routed experts; with kTilesShared, the shared expert alone)
 hipError_t launch_grouped_up256(const GroupedGemmArgs& args, hipStream_t stream);
 hipError_t launch_grouped_down256(const GroupedGemmArgs& args, hipStream_t stream);
 
