@@ -160,15 +160,12 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& a, const Tile& 
         const int64_t k0 = static_cast<int64_t>(k) * BK;
 #pragma unroll
         for (int i = 0; i < AP; ++i) ra[i] = *reinterpret_cast<const u32x4*>(arow[i] + k0);
-        const int64_t g = k0 / kGroup;
-        const int quarter = k & 3;
         if (ROUTED) {
-            rb[0] = *reinterpret_cast<const u32x4*>(bq + g * 1024 + quarter * 256);
-            rs = bs[g * 16 * a.spt + ((quarter * a.spt) >> 2)];
+            rb[0] = *reinterpret_cast<const u32x4*>(bq + k * 256);
+            rs = bs[step_scale(k, a.spt)];
         } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                rb[c] = *reinterpret_cast<const u32x4*>(bh[c] + g * 2048 + quarter * 512);
+            for (int c = 0; c < 4; ++c) rb[c] = *reinterpret_cast<const u32x4*>(bh[c] + k * 512);
         }
     };
     // registers -> LDS stage (int4 B dequantized on the way)

@@ -119,15 +119,12 @@ __device__ __forceinline__ void gemm256_tile(const GroupedGemmArgs& a, const Til
         const int64_t k0 = static_cast<int64_t>(k) * BK2;
 #pragma unroll
         for (int i = 0; i < AP; ++i) ra[i] = *reinterpret_cast<const u32x4*>(arow[i] + k0);
-        const int64_t g = k0 / kGroup;
-        const int quarter = k & 3;
         if (ROUTED) {
-            rb[0] = *reinterpret_cast<const u32x4*>(bq + g * 1024 + quarter * 256);
-            rs = bs[g * 16 * a.spt + ((quarter * a.spt) >> 2)];
+            rb[0] = *reinterpret_cast<const u32x4*>(bq + k * 256);
+            rs = bs[step_scale(k, a.spt)];
         } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                rb[c] = *reinterpret_cast<const u32x4*>(bh[c] + g * 2048 + quarter * 512);
+            for (int c = 0; c < 4; ++c) rb[c] = *reinterpret_cast<const u32x4*>(bh[c] + k * 512);
         }
     };
     auto store_step = [&](const u32x4 (&ra)[AP], const u32x4 (&rb)[BV], float rs, int stage)
@@ -192,8 +189,6 @@ __device__ __forceinline__ void gemm256_tile(const GroupedGemmArgs& a, const Til
         uint8_t* ws_st = lds + wr * STAGE2;
         const int kn = (k + 4) < steps ? k + 4 : steps - 1;  // the step requested next
         const int64_t kn0 = static_cast<int64_t>(kn) * BK2;
-        const int64_t gn = kn0 / kGroup;
-        const int qn = kn & 3;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             // chunk i: A sub-tile i against all 8 B fragments (full tile), or
@@ -219,13 +214,12 @@ __device__ __forceinline__ void gemm256_tile(const GroupedGemmArgs& a, const Til
                         dequant8(rb[0][piece], rs);
                 } else {
                     *reinterpret_cast<u32x4*>(ws_st + b_st_h + piece * SUB2) = rb[ROUTED ? 0 : piece];
-                    rb[ROUTED ? 0 : piece] =
-                        *reinterpret_cast<const u32x4*>(bh[piece] + gn * 2048 + qn * 512);
+                    rb[ROUTED ? 0 : piece] = *reinterpret_cast<const u32x4*>(bh[piece] + kn * 512);
                 }
             }
             if (ROUTED && i == 7) {
-                rb[0] = *reinterpret_cast<const u32x4*>(bq + gn * 1024 + qn * 256);
-                rs = bs[gn * 16 * a.spt + ((qn * a.spt) >> 2)];
+                rb[0] = *reinterpret_cast<const u32x4*>(bq + kn * 256);
+                rs = bs[step_scale(kn, a.spt)];
             }
             // MFMAs paced with the chunk's other work
             if (ROUTED && (i & 1)) {

@@ -78,6 +78,15 @@ inline unsigned xcd_grid(int64_t max_tiles, int64_t wr) {
     return static_cast<unsigned>(8 * ((max_tiles * wmax + 8 * wmin - 1) / (8 * wmin) + 1));
 }
 
+// A 128-column group spans four 32-wide reduction steps, so step k of a
+// 16-row tile column starts k * 256 bytes (int4: 1 KB tiles) or k * 512 bf16
+// elements (4 KB tiles) after its first tile, and its int4 scale (128 / group
+// per tile row: spt) step_scale(k, spt) floats after the row's first.
+static_assert(kGroup == 128, "four 32-wide steps per group");
+__device__ __forceinline__ int step_scale(int k, int spt) {
+    return (k >> 2) * 16 * spt + (((k & 3) * spt) >> 2);
+}
+
 // 8 int4 codes (one 32-bit word) times scale -> 4 packed bf16 pairs (RNE)
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
