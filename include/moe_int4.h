@@ -56,10 +56,11 @@ enum moe_path {
                               PREFILL_WIDE */
     MOE_PATH_PREFILL = 1,  /* grouped GEMMs on MFMA for every expert, 128-row tiles */
     MOE_PATH_DECODE = 2,   /* HBM-streaming GEMV over the touched experts */
-    MOE_PATH_HYBRID = 3,   /* grouped GEMMs for the shared expert and for routed experts with
-                              more than 32 pairs; routed experts with 1..32 pairs on the
+    MOE_PATH_HYBRID = 3,   /* grouped GEMMs for routed experts with more than 32 pairs
+                              (128-row tiles) and for the shared expert (256-row tiles, a
+                              launch of its own); routed experts with 1..32 pairs on the
                               streaming kernel, which reads their weights once instead of
-                              padding them to 128-row GEMM tiles */
+                              padding them to GEMM tiles */
     MOE_PATH_PREFILL_WIDE = 4  /* PREFILL with 256 x 256 tiles (one block per CU, twice the
                               MFMA work per fragment read); pays off when experts hold
                               hundreds of rows */
