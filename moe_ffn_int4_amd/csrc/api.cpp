@@ -624,10 +624,10 @@ static int forward_impl(const moe_dims* dims, const uint16_t* x, const float* ro
 
     const bool decode =
         path == MOE_PATH_DECODE || (path == MOE_PATH_AUTO && P <= kDecodeMaxPairs);
-    // decode path, int4 groups of 128 without sliced staging (P < 4 E): the down
+    // decode path, int4 experts without sliced staging (P < 4 E): the down
     // projection splits its reduction over two blocks per chunk (twice the blocks
     // of a launch that otherwise leaves HBM underused), the second half into O2
-    float* O2 = (decode && ex4 && d.group_size == moe::kGroup && P < 4 * d.E &&
+    float* O2 = (decode && ex4 && P < 4 * d.E &&
                  P + d.T <= kSplitRows && d.h >= 2 * moe::kGroup)
                     ? reinterpret_cast<float*>(base + L.O2) : nullptr;
     const bool hybrid = !decode && (path == MOE_PATH_HYBRID ||

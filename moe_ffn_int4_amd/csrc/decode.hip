@@ -378,13 +378,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const int64_t K = a.K, N = a.N;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kq = lane >> 4;
-    // Reduction split (the host's second output, down projection, int4 groups
-    // of 128; the same condition as the launcher): the two halves of a
+    // Reduction split (the host's second output, down projection, int4 weights
+    // of any group size; the same condition as the launcher): the two halves of a
     // feature range are adjacent blocks in x, so the blocks dispatched
     // together read both halves of the same row blocks of the weights
     // (measured on the Scout decode layer: down 54.7 -> 52.8 us against
     // halves in grid z).
-    const int nkz = (!UP && !F8 && !SL && S == 1 && a.o_out2) ? 2 : 1;
+    const int nkz = (!UP && !F8 && !SL && a.o_out2) ? 2 : 1;
     const int kz = static_cast<int>(blockIdx.x) % nkz;
     const int64_t n = static_cast<int64_t>(blockIdx.x / nkz) * 64 + (narrow ? wave : sub) * 16 + l16;  // B column
     const int ng = static_cast<int>(K / kGroup);
@@ -712,9 +712,9 @@ static hipError_t launch_decode(const DecodeArgs& args, int max_chunks, int shar
     constexpr size_t sliced = SL ? slice_lds_bytes(slice_groups(UP, DL)) : 0;
     if (a.lds_rows < kDecodeRows && lds < sliced) lds = sliced;
     // two blocks per chunk and feature range, each half the reduction, when the
-    // host gives a second output (down projection, int4 groups of 128); the
+    // host gives a second output (down projection, int4 weights); the
     // kernel takes the half from blockIdx.x under the same condition
-    const unsigned zs = (!UP && !F8 && !SL && S == 1 && a.o_out2) ? 2u : 1u;
+    const unsigned zs = (!UP && !F8 && !SL && a.o_out2) ? 2u : 1u;
     dim3 grid(static_cast<unsigned>(a.N / 64 * zs), static_cast<unsigned>(max_chunks + 3 * shared_chunks), 1);
     MOE_LAUNCH((decode_kernel<UP, DR, DS, DL, F8, S, SL>), grid, dim3(NT), lds, stream, a);
     return hipGetLastError();
@@ -739,9 +739,14 @@ hipError_t launch_decode_up(const DecodeArgs& args, int max_chunks, int shared_c
 hipError_t launch_decode_down(const DecodeArgs& args, int max_chunks, int shared_chunks,
                               hipStream_t stream) {
     if (args.wf0) return launch_decode<false, 3, 2, 7, true, 1>(args, max_chunks, shared_chunks, stream);
-    if (args.spt == 2) return launch_decode<false, 3, 2, 7, false, 2>(args, max_chunks, shared_chunks, stream);
-    if (args.spt == 4) return launch_decode<false, 2, 2, 5, false, 4>(args, max_chunks, shared_chunks, stream);
+    if (args.spt == 2) return launch_decode<false, 2, 2, 5, false, 2>(args, max_chunks, shared_chunks, stream);
+    if (args.spt == 4) return launch_decode<false, 2, 2, 2, false, 4>(args, max_chunks, shared_chunks, stream);
     if (args.sliced) return launch_decode<false, 3, 2, 7, false, 1, true>(args, max_chunks, shared_chunks, stream);
+    // Groups of 64 and 32 with the reduction split (Scout decode layer, three
+    // alternating rounds): down 63.2 -> 58.1 us and 68.8 -> 60.2 us against
+    // the unsplit launch at rings (3, 7) and (2, 5); LDS rings of 4 (groups of
+    // 64) and 3 (groups of 32), or a global ring of 3 at groups of 32 (68.8 us),
+    // measured slower.
     // LDS ring 5 (7 before the reduction split halved each block's groups: 53.0
     // against 54.2 us on the Scout decode layer)
     return launch_decode<false, 3, 2, 5, false, 1>(args, max_chunks, shared_chunks, stream);
