@@ -89,12 +89,24 @@ __device__ __forceinline__ int step_scale(int k, int spt) {
 
 // 8 int4 codes (one 32-bit word) times scale -> 4 packed bf16 pairs (RNE)
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s) {
+    // The sign bit of every nibble flipped gives u = code + 8 in 0..15; the
+    // even nibbles go to bytes 0..3 of lo, the odd ones to those of hi. The
+    // fma forms u * s - 8 s with one rounding: the exact value is code * s
+    // (8 s is exact), so each result is the fp32 product code * s.
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t x = w ^ 0x88888888u;
+    uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+    // opaque to the optimizer, so each byte converts with v_cvt_f32_ubyte0..3
+    // instead of a 4-bit field extract and a conversion
+    asm("" : "+v"(lo), "+v"(hi));
+    const float off = -8.0f * s;
     uint32_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const bf16x2 v = {static_cast<__bf16>(static_cast<float>(nib(w, 2 * j)) * s),
-                          static_cast<__bf16>(static_cast<float>(nib(w, 2 * j + 1)) * s)};
+        const float a = static_cast<float>((lo >> (8 * j)) & 0xFFu);
+        const float b = static_cast<float>((hi >> (8 * j)) & 0xFFu);
+        const bf16x2 v = {static_cast<__bf16>(__builtin_fmaf(a, s, off)),
+                          static_cast<__bf16>(__builtin_fmaf(b, s, off))};
         o[j] = __builtin_bit_cast(uint32_t, v);
     }
     return u32x4{o[0], o[1], o[2], o[3]};
