@@ -92,7 +92,9 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s) {
     // The sign bit of every nibble flipped gives u = code + 8 in 0..15; the
     // even nibbles go to bytes 0..3 of lo, the odd ones to those of hi. The
     // fma forms u * s - 8 s with one rounding: the exact value is code * s
-    // (8 s is exact), so each result is the fp32 product code * s.
+    // (8 s is exact), so each result is the fp32 product code * s (for the
+    // quantizer's positive scales bit for bit; a zero or negative scale can
+    // turn a -0 product into +0).
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const uint32_t x = w ^ 0x88888888u;
     uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
