@@ -12,8 +12,8 @@
 // which rounds to the nearest OCP E4M3 value, ties to even.
 //
 // One block per row: the row maximum is reduced across the block, then the
-// row is read again (from L2) and converted, 4 consecutive values per thread
-// (one 32-bit store of 4 codes). HBM-bound: weights read 4 B and write 1 B
+// row is converted, 4 consecutive values per thread (one 32-bit store of 4
+// codes), from registers where the row fits them, else read again (from L2). HBM-bound: weights read 4 B and write 1 B
 // per value (+ 4 B per row); activations read 2 B and write 1 B.
 //
 // Weight codes go to the tiled order the forward pass reads: tile
@@ -41,30 +41,46 @@ __device__ __forceinline__ float4 load4(const uint16_t* p) {
 }  // namespace
 
 // SRC = float (weights, tiled codes) or uint16_t (bf16 activations, row-major
-// codes); ub > 0 bounds the row maximum
-template <typename SRC, bool TILED>
-__global__ __launch_bounds__(NT) void quantize_fp8_rows_kernel(const SRC* __restrict__ src, int64_t K,
+// codes); ub > 0 bounds the row maximum. NB threads per row; rows of at most
+// 4 * NB * R values keep their values in registers between the two passes,
+// longer rows read them again (from L2).
+template <typename SRC, bool TILED, int NB, int R>
+__global__ __launch_bounds__(NB) void quantize_fp8_rows_kernel(const SRC* __restrict__ src, int64_t K,
                                                                float ub, uint8_t* __restrict__ q,
                                                                float* __restrict__ scales) {
-    __shared__ float red[NT / 64];
+    constexpr int NW = NB / 64;
+    __shared__ float red[NW];
     const int64_t row = blockIdx.x;
     const SRC* r = src + row * K;
     const int tid = threadIdx.x;
+    const bool held = K <= 4 * NB * R;
+    float4 hv[R];
     float m = 0.f;
-    for (int64_t k = 4 * tid; k < K; k += 4 * NT) {
-        const float4 v = load4(r + k);
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    if (held) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int64_t k = 4 * (tid + i * NB);
+            hv[i] = k < K ? load4(r + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(hv[i].x), fabsf(hv[i].y)),
+                               fmaxf(fabsf(hv[i].z), fabsf(hv[i].w))));
+        }
+    } else {
+        for (int64_t k = 4 * tid; k < K; k += 4 * NB) {
+            const float4 v = load4(r + k);
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
     }
     m = wave_max(m);
     if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    m = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) m = fmaxf(m, red[i]);
     m = fmaxf(m, kTiny);
     if (ub > 0.f) m = fminf(m, ub);
     const float s = m / kFp8Max;
     if (tid == 0) scales[row] = s;
-    for (int64_t k = 4 * tid; k < K; k += 4 * NT) {
-        const float4 v = load4(r + k);
+    auto put = [&](const float4 v, int64_t k) __attribute__((always_inline)) {
         const float a = fminf(fmaxf(v.x / s, -kFp8Max), kFp8Max);
         const float b = fminf(fmaxf(v.y / s, -kFp8Max), kFp8Max);
         const float c = fminf(fmaxf(v.z / s, -kFp8Max), kFp8Max);
@@ -79,22 +95,33 @@ __global__ __launch_bounds__(NT) void quantize_fp8_rows_kernel(const SRC* __rest
             at = row * K + k;
         }
         *reinterpret_cast<int*>(q + at) = w;
+    };
+    if (held) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int64_t k = 4 * (tid + i * NB);
+            if (k < K) put(hv[i], k);
+        }
+    } else {
+        for (int64_t k = 4 * tid; k < K; k += 4 * NB) put(load4(r + k), k);
     }
 }
 
 hipError_t launch_quantize_fp8_weights(const float* w, int64_t rows, int64_t K, uint8_t* q,
                                        float* scales, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
-    MOE_LAUNCH((quantize_fp8_rows_kernel<float, true>), dim3(static_cast<unsigned>(rows)),
+    MOE_LAUNCH((quantize_fp8_rows_kernel<float, true, NT, 1>), dim3(static_cast<unsigned>(rows)),
                        dim3(NT), 0, stream, w, K, 0.f, q, scales);
     return hipGetLastError();
 }
 
+// activations: a few rows per call on the decode path, so 1024 threads per
+// row and the row held in registers (K <= 8192)
 hipError_t launch_quantize_fp8_activations(const uint16_t* x, int64_t rows, int64_t K, float ub,
                                            uint8_t* q, float* scales, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
-    MOE_LAUNCH((quantize_fp8_rows_kernel<uint16_t, false>), dim3(static_cast<unsigned>(rows)),
-                       dim3(NT), 0, stream, x, K, ub, q, scales);
+    MOE_LAUNCH((quantize_fp8_rows_kernel<uint16_t, false, 1024, 2>), dim3(static_cast<unsigned>(rows)),
+                       dim3(1024), 0, stream, x, K, ub, q, scales);
     return hipGetLastError();
 }
 
