@@ -82,20 +82,17 @@ def parse():
     return a
 
 
-STAGE_TRAFFIC_KEY = {"decode_up": "decode_up", "grouped_up": "grouped_up"}
-
-
 def measured_traffic(stage: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (profiles/traffic.json), or None if there is none for this kernel and
-    workload or a source file of the kernel or its launch changed since the
-    counters were taken."""
+    """HBM bytes per launch of a stage on a workload from the committed
+    rocprofv3 counter summary (profiles/traffic.json, records keyed
+    "<stage>@<workload>"; a stage whose launch runs several kernels sums them),
+    or None if there is no record or a source file of its kernels or their
+    launch changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    key = STAGE_TRAFFIC_KEY.get(stage)
-    if key is None or not os.path.exists(path):
+    if workload is None or not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(key)
+    rec = json.load(open(path)).get(f"{stage}@{workload}")
     if not rec or rec.get("workload") != workload:
         return None
     # every file that defines the kernel or its launch must be as profiled
