@@ -66,3 +66,29 @@ def test_group_and_format_bytes():
     # fp8 row-wise: one byte per weight and one fp32 scale per row
     u8 = bench.stage_units(cfg, counts, experts="fp8")
     assert u8["step_bytes"] == 3 * d * h + (2 * h + d) * 4 + base
+
+
+def test_traffic_record_tracks_its_sources(tmp_path, monkeypatch):
+    """A counter record is reported only for its own stage and workload and
+    only while every source file it names is byte-identical to the one
+    measured; any edit of a source turns the field to null."""
+    import hashlib
+    import json
+    src = tmp_path / "moe_ffn_int4_amd" / "csrc" / "k.hip"
+    src.parent.mkdir(parents=True)
+    src.write_text("kernel as profiled\n")
+    (tmp_path / "profiles").mkdir()
+    rec = {"stage": "grouped_up", "workload": "scout_prefill", "hbm_bytes_per_launch": 123.0,
+           "sources_sha256": {"moe_ffn_int4_amd/csrc/k.hip":
+                              hashlib.sha256(src.read_bytes()).hexdigest()}}
+    (tmp_path / "profiles" / "traffic.json").write_text(
+        json.dumps({"grouped_up@scout_prefill": rec}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("grouped_up", "scout_prefill") == 123.0
+    assert bench.measured_traffic("grouped_up", "wide_routing") is None
+    assert bench.measured_traffic("decode_up", "scout_prefill") is None
+    assert bench.measured_traffic("grouped_up", None) is None
+    src.write_text("kernel as profiled, then edited\n")
+    assert bench.measured_traffic("grouped_up", "scout_prefill") is None
+    src.unlink()
+    assert bench.measured_traffic("grouped_up", "scout_prefill") is None
