@@ -545,8 +545,8 @@ def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one MI355X: this build runs on a single GPU; "
-              "--gpus must be 1 (multi-GPU expert parallelism is design-only here).",
+        print("bench.py measures one MI355X: the library runs on a single GPU; "
+              "--gpus must be 1 (expert parallelism across GPUs is a design, not implemented).",
               file=sys.stderr)
         return 2
 
