@@ -12,7 +12,8 @@ Steps cycle through ``--layers`` independently seeded copies of the layer (as
 consecutive layers of a model would), so a step streams weights that are not
 in the 256 MB last-level cache from the step before.
 
-Prints ONE JSON line: the driver's fields plus
+Prints ONE JSON line: metric, value, unit, n_gpus, steps, warmup, ms_per_step,
+higher_is_better, scaling, vs_baseline, dtype, data and config, plus
   roofline      the dominant kernel: algorithmic bytes (or FLOPs) per launch
                 divided by its mean launch time, from HIP events the kernels
                 record at their own start and end (a second, eager pass over

@@ -249,6 +249,6 @@ int main(void)
     bad |= run_layer(256, 384, 4, 2, 64);   /* groups of 64, h not a power of two */
     bad |= run_layer(128, 256, 5, 5, 32);   /* groups of 32, top_k = E */
     bad |= run_layer(256, 128, 6, 1, 128);  /* h < d */
-    if (!bad) printf("oracle sanitize driver: all calls clean\n");
+    if (!bad) printf("oracle sanitize run: all calls clean\n");
     return bad;
 }
