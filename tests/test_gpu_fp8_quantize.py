@@ -32,11 +32,16 @@ def test_weights_tiled(rows, K):
         assert qb[t * 2048 + ((k % 128) // 32) * 512 + (r % 16) * 32 + k % 32] == c_ref[r, k]
 
 
+# The launch takes 1024-thread rows below 512 rows and 256-thread rows from
+# 512 on; either holds a row of up to 8192 values in registers and reads a
+# longer one twice. These shapes reach all four forms and both sides of 512.
+@pytest.mark.parametrize("rows,K", [(37, 5120), (37, 8320), (511, 1024), (512, 1024),
+                                    (600, 5120), (600, 8320)])
 @pytest.mark.parametrize("ub", [1200.0, 2.5, 0.0])
-def test_activations_rows(ub):
-    say(f"fp8 activations: ub={ub}")
-    rng = np.random.default_rng(7)
-    x = torch.from_numpy(rng.standard_normal((37, 5120)).astype(np.float32) * 1.5).to(torch.bfloat16)
+def test_activations_rows(ub, rows, K):
+    say(f"fp8 activations: ub={ub} rows={rows} K={K}")
+    rng = np.random.default_rng(7 + rows + K)
+    x = torch.from_numpy(rng.standard_normal((rows, K)).astype(np.float32) * 1.5).to(torch.bfloat16)
     x[4] = 0.0
     x[6, 100] = 40.0  # above a small bound: saturates there
     q, s = moe.quantize_fp8_rows(x.to(DEV), ub)
